@@ -1,0 +1,283 @@
+"""CPU oracle for the Forcing-KV hybrid head-wise KV-cache compression path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this module.  It shares no
+code with the HIP library (``hybrid_kv_cache_amd``) and neither side imports
+the other; the seeded input generator is the only thing both use.
+
+Everything here is plain NumPy in float64, written step by step in the order
+the method takes them, with no blocking, fusion or reordering beyond what the
+definitions state.  Sources (pages on the method):
+
+  [S] "Forcing-KV：面向高效自回归视频扩散模型的混合KV缓存压缩" (ai-feeds.com
+      summary of arXiv 2605.09681), section 方法 (Method):
+        › 输入与整体流程 (input and overall flow)   -> per-layer, per-frame cache
+        › 关键模块 › 2 静态结构剪枝 (static structural pruning) -> select_static
+        › 关键模块 › 3 动态相似性剪枝 (dynamic similarity pruning) -> scoring,
+          select_dynamic
+        › 输出与工程收益 (output)  -> compact, attend
+  [A] "Forcing-KV: Hybrid KV Cache Compression for Efficient Autoregressive
+      Video Diffusion Models" (tomesphere.com), Abstract: static heads get
+      structured static pruning, dynamic heads get pruning by segment-wise
+      similarity.
+
+Where the pages leave a step open, the reading taken is stated at the function
+(scoring rule: softmax attention mass per frame from a strided sample of the
+current chunk's queries, over the whole window including the current chunk;
+ranking ties broken by the lower frame index; kept frames in ascending order,
+the current chunk last; non-causal attention with scale 1/sqrt(D)).
+
+Pinned by tests/test_oracle_pins.py (invariants, closed forms, brute force,
+library cross-checks).  Parity of generic numeric outputs is otherwise
+pinned only through those checks; no page prints a worked example.
+
+Layouts (token-major):  q [Nq, H, D];  k, v [N_win, H, D] with the window's
+frames oldest first and the current chunk's ``F_c`` frames last.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+STATIC = 0
+DYNAMIC = 1
+TIE_REL = 1e-5
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    u32 = bits.astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Inputs come as float32 values or bf16 bit patterns; both convert exactly."""
+    if x.dtype == np.uint16:
+        return decode_bf16(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def logit_scale(head_dim: int, scale: float = 0.0) -> float:
+    """Softmax temperature: 1/sqrt(D) unless the caller gives one (the pages
+    are silent; standard scaled dot-product attention is assumed)."""
+    return float(scale) if scale else 1.0 / math.sqrt(head_dim)
+
+
+def sampled_query_rows(n_q: int, stride: int) -> np.ndarray:
+    """The strided query sample used for scoring: rows 0, s, 2s, ... < Nq."""
+    return np.arange(0, n_q, stride, dtype=np.int64)
+
+
+def frame_masses(q_h: np.ndarray, k_h: np.ndarray, tokens_per_frame: int,
+                 stride: int, scale: float) -> np.ndarray:
+    """Attention mass each window frame receives from each sampled query of one
+    head.  [S] 关键模块 › 3: the history cache is grouped by frame and each group
+    is scored by attention against the current queries.
+
+    q_h [Nq, D], k_h [N_win, D] in float64.  For each sampled query i:
+      z_j = scale * q_i . k_j            for every window key j
+      p   = softmax(z)                   over the WHOLE window (history and
+                                         the current chunk alike)
+      mass[i, f] = sum of p_j over the T tokens of frame f
+    Returns mass [n_s, F_total].
+    """
+    rows = sampled_query_rows(q_h.shape[0], stride)
+    n_win = k_h.shape[0]
+    n_frames = n_win // tokens_per_frame
+    z = (q_h[rows] @ k_h.T) * scale
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p.reshape(len(rows), n_frames, tokens_per_frame).sum(axis=2)
+
+
+def segment_scores(q: np.ndarray, k: np.ndarray, head_role: np.ndarray,
+                   tokens_per_frame: int, hist_frames: int, stride: int,
+                   scale: float = 0.0) -> np.ndarray:
+    """Per-head score of every history frame.  [S] 关键模块 › 3.
+
+    Dynamic head h: score[h, f] = mean over the sampled queries of mass[i, f],
+    for the history frames f < F_h.  Static heads are not scored (NaN).
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    H, D = q.shape[1], q.shape[2]
+    sc = logit_scale(D, scale)
+    out = np.full((H, hist_frames), np.nan, dtype=np.float64)
+    for h in range(H):
+        if head_role[h] != DYNAMIC or hist_frames == 0:
+            continue
+        mass = frame_masses(q[:, h, :], k[:, h, :], tokens_per_frame, stride, sc)
+        out[h] = mass[:, :hist_frames].mean(axis=0)
+    return out
+
+
+def select_static(mask_row: np.ndarray) -> np.ndarray:
+    """[S] 关键模块 › 2: a static head keeps the fixed, profiled positions,
+    taken by mask.  Frame granular: the kept history frames are those whose
+    mask entry is set, in ascending order."""
+    return np.flatnonzero(np.asarray(mask_row) != 0).astype(np.int64)
+
+
+def select_dynamic(score_row: np.ndarray, budget_m: int) -> np.ndarray:
+    """[S] 关键模块 › 3: keep the few best-scoring frames.  The m_eff = min(m, F_h)
+    frames ranked first by (score descending, frame index ascending), returned
+    in ascending frame order."""
+    f_h = len(score_row)
+    m_eff = min(budget_m, f_h)
+    order = sorted(range(f_h), key=lambda f: (-score_row[f], f))
+    return np.array(sorted(order[:m_eff]), dtype=np.int64)
+
+
+def select_frames(scores: np.ndarray, head_role: np.ndarray,
+                  static_keep_mask: np.ndarray, budget_m: int) -> List[np.ndarray]:
+    """Kept history frames per head ([A]: static heads by structure, dynamic
+    heads by segment similarity)."""
+    if budget_m < 0:
+        raise ValueError("budget_m must be >= 0")
+    kept = []
+    for h in range(len(head_role)):
+        if head_role[h] == DYNAMIC:
+            kept.append(select_dynamic(scores[h], budget_m))
+        else:
+            kept.append(select_static(static_keep_mask[h]))
+    return kept
+
+
+def offsets(kept: Sequence[np.ndarray], tokens_per_frame: int, cur_frames: int):
+    """Ragged layout bookkeeping.  seg_idx = the kept history frames of head 0,
+    then head 1, ...; seg_off[h] = where head h's frames start in seg_idx;
+    tok_off[h] = first compacted row of head h, each head holding its kept
+    history frames followed by the current chunk."""
+    H = len(kept)
+    seg_off = np.zeros(H + 1, dtype=np.int64)
+    tok_off = np.zeros(H + 1, dtype=np.int64)
+    for h in range(H):
+        seg_off[h + 1] = seg_off[h] + len(kept[h])
+        tok_off[h + 1] = tok_off[h] + (len(kept[h]) + cur_frames) * tokens_per_frame
+    seg_idx = (np.concatenate(kept) if H and seg_off[H] else np.zeros(0)).astype(np.int64)
+    return seg_idx, seg_off, tok_off
+
+
+def compact(k: np.ndarray, v: np.ndarray, kept: Sequence[np.ndarray],
+            tokens_per_frame: int, hist_frames: int, cur_frames: int):
+    """[S] 输出与工程收益: the compressed K/V that replace the cache in attention.
+
+    Head-major ragged rows: for head h, the T rows of each kept history frame
+    (ascending), then the T rows of each current-chunk frame.  A pure copy:
+    values are returned in the input's own dtype, unchanged.
+    Returns k_c, v_c [tok_off[H], D] and the offsets.
+    """
+    T = tokens_per_frame
+    seg_idx, seg_off, tok_off = offsets(kept, T, cur_frames)
+    H, D = k.shape[1], k.shape[2]
+    k_c = np.empty((int(tok_off[H]), D), dtype=k.dtype)
+    v_c = np.empty((int(tok_off[H]), D), dtype=v.dtype)
+    for h in range(H):
+        frames = list(kept[h]) + list(range(hist_frames, hist_frames + cur_frames))
+        row = int(tok_off[h])
+        for f in frames:
+            k_c[row:row + T] = k[f * T:(f + 1) * T, h, :]
+            v_c[row:row + T] = v[f * T:(f + 1) * T, h, :]
+            row += T
+    return k_c, v_c, seg_idx, seg_off, tok_off
+
+
+def softmax_attention(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                      scale: float) -> np.ndarray:
+    """Textbook attention of a block of queries over a set of keys, float64:
+    softmax(scale * q k^T) v, non-causal."""
+    z = (q_rows @ k_rows.T) * scale
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=1, keepdims=True)) @ v_rows
+
+
+def attend(q: np.ndarray, k_c: np.ndarray, v_c: np.ndarray, tok_off: np.ndarray,
+           scale: float = 0.0, rows: Optional[np.ndarray] = None,
+           block: int = 1024) -> np.ndarray:
+    """[S] 输出与工程收益: the current chunk's queries attend over the compressed
+    cache.  Every query of head h sees all of head h's compacted rows (kept
+    history frames and the current chunk); no causal mask inside the window.
+
+    rows: optional subset of query indices (for large cases); returns
+    [len(rows) or Nq, H, D] float64.
+    """
+    qf = as_f64(q)
+    kc = as_f64(k_c)
+    vc = as_f64(v_c)
+    H, D = qf.shape[1], qf.shape[2]
+    sc = logit_scale(D, scale)
+    sel = np.arange(qf.shape[0]) if rows is None else np.asarray(rows)
+    out = np.empty((len(sel), H, D), dtype=np.float64)
+    for h in range(H):
+        lo, hi = int(tok_off[h]), int(tok_off[h + 1])
+        for b in range(0, len(sel), block):
+            r = sel[b:b + block]
+            out[b:b + block, h] = softmax_attention(qf[r, h], kc[lo:hi], vc[lo:hi], sc)
+    return out
+
+
+def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float = 0.0,
+                 rows: Optional[np.ndarray] = None, block: int = 1024) -> np.ndarray:
+    """Full-KV baseline: every query attends over the whole uncompressed window."""
+    qf = as_f64(q)
+    kf = as_f64(k)
+    vf = as_f64(v)
+    H, D = qf.shape[1], qf.shape[2]
+    sc = logit_scale(D, scale)
+    sel = np.arange(qf.shape[0]) if rows is None else np.asarray(rows)
+    out = np.empty((len(sel), H, D), dtype=np.float64)
+    for h in range(H):
+        for b in range(0, len(sel), block):
+            r = sel[b:b + block]
+            out[b:b + block, h] = softmax_attention(qf[r, h], kf[:, h], vf[:, h], sc)
+    return out
+
+
+def compress(q, k, v, head_role, static_keep_mask, budget_m: int,
+             tokens_per_frame: int, hist_frames: int, cur_frames: int,
+             query_stride: int, scale: float = 0.0) -> Dict[str, np.ndarray]:
+    """The whole compression step of one layer: score, select, compact."""
+    scores = segment_scores(q, k, head_role, tokens_per_frame, hist_frames,
+                            query_stride, scale)
+    kept = select_frames(scores, head_role, static_keep_mask, budget_m)
+    k_c, v_c, seg_idx, seg_off, tok_off = compact(k, v, kept, tokens_per_frame,
+                                                  hist_frames, cur_frames)
+    return dict(scores=scores, kept=kept, k_c=k_c, v_c=v_c, seg_idx=seg_idx,
+                seg_off=seg_off, tok_off=tok_off)
+
+
+def cutoff_band(score_row: np.ndarray, budget_m: int, rel: float = TIE_REL):
+    """Frames whose membership in the top-m set is decided by a near tie.
+
+    When the m_eff-th and the (m_eff+1)-th best scores differ by at most
+    ``rel`` relative, every frame whose score lies within ``rel`` (relative)
+    of the m_eff-th best is ambiguous: another exact arithmetic order may keep
+    any m_eff-sized set that holds all frames above the band and none below.
+    Returns (sure_keep, band, sure_drop) as sets of frame indices.
+    """
+    f_h = len(score_row)
+    m_eff = min(budget_m, f_h)
+    order = sorted(range(f_h), key=lambda f: (-score_row[f], f))
+    if m_eff == 0 or m_eff == f_h:
+        return set(order[:m_eff]), set(), set(order[m_eff:])
+    s_m, s_n = score_row[order[m_eff - 1]], score_row[order[m_eff]]
+    if abs(s_m - s_n) > rel * max(abs(s_m), abs(s_n)):
+        return set(order[:m_eff]), set(), set(order[m_eff:])
+    band = {f for f in range(f_h)
+            if abs(score_row[f] - s_m) <= rel * max(abs(score_row[f]), abs(s_m))}
+    keep = {f for f in order[:m_eff] if f not in band}
+    drop = {f for f in order[m_eff:] if f not in band}
+    return keep, band, drop
+
+
+def kept_set_valid(candidate: Sequence[int], score_row: np.ndarray, budget_m: int,
+                   rel: float = TIE_REL) -> bool:
+    """Whether a kept set agrees with the oracle up to the cutoff tie band."""
+    keep, band, drop = cutoff_band(score_row, budget_m, rel)
+    g = set(int(x) for x in candidate)
+    m_eff = min(budget_m, len(score_row))
+    return len(g) == m_eff and keep <= g and not (g & drop) and g <= (keep | band)
