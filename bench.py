@@ -1,0 +1,228 @@
+"""Benchmark of the Forcing-KV hot path on one MI355X.
+
+One step = one pass of the whole path over one attention layer: fkv_compress
+(score dynamic heads, select frames, compact K/V) then fkv_attend (the
+current chunk's queries over the compressed cache).  Inputs are seeded
+synthetic tensors already resident in HBM.  The default workload is the
+480P single layer (12 heads, D=128, 1560 tokens per latent frame, 18 history
++ 3 current frames, m=13, every 16th query scored); the 1080P layer is
+measured too and reported under "secondary".
+
+To keep the 256 MB last-level cache from holding a 480P layer's whole window
+between steps, the timed loop walks over several device copies of the layer
+(--copies), so K/V come from HBM as they would in a multi-layer pass.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+METRIC = "compressed-attn query tok/s per layer @480P/1080P; % MFMA & HBM roofline"
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="480p_layer")
+    ap.add_argument("--secondary", default="1080p_layer",
+                    help="second workload to report ('' to skip)")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run the timed loop only (for rocprofv3), print nothing else")
+    return ap.parse_args()
+
+
+class Layer:
+    """Device state of one layer (inputs + compressed cache + outputs).  With
+    `src`, the inputs are device copies of another Layer's."""
+
+    def __init__(self, w, inp, fkv, torch, src=None):
+        self.w = w
+        if src is None:
+            self.q, self.k, self.v = (fkv.to_device(inp.q), fkv.to_device(inp.k),
+                                      fkv.to_device(inp.v))
+        else:
+            self.q, self.k, self.v = src.q.clone(), src.k.clone(), src.v.clone()
+        self.role, self.mask = inp.head_role, inp.static_keep_mask
+        self.desc = fkv.desc_for(w)
+        self.ckv = fkv.CompressedKV(self.desc, self.role, self.mask, w.budget_m)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=dt, device="cuda")
+        self.dout = torch.empty_like(self.out)
+
+
+def time_loop(fn, layers, steps, warmup, torch):
+    """Mean ms per call of fn(layer), cycling through layers; events on the
+    stream the kernels are launched on (torch's current stream)."""
+    for i in range(warmup):
+        fn(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(layers[i % len(layers)])
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def measure(wname, args, fkv, torch, W):
+    w = W.WORKLOADS[wname]
+    inp = W.generate_layer(w, 0)
+    base = Layer(w, inp, fkv, torch)
+    layers = [base] + [Layer(w, inp, fkv, torch, src=base) for _ in range(max(args.copies, 1) - 1)]
+
+    def step(L):
+        fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
+        fkv.fkv_attend(L.desc, L.q, L.ckv, L.out)
+
+    ms_step = time_loop(step, layers, args.steps, args.warmup, torch)
+    if args.profile_only:
+        return None
+    ms_compress = time_loop(lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
+                                                       w.budget_m, L.ckv),
+                            layers, args.steps, args.warmup, torch)
+    ms_attend = time_loop(lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv, L.out),
+                          layers, args.steps, args.warmup, torch)
+    ms_dense = time_loop(lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout),
+                         layers, args.steps, args.warmup, torch)
+    kept = base.ckv.kept_tokens
+    D = w.head_dim
+    attn_flop = 4.0 * w.n_q * D * kept
+    dense_flop = 4.0 * w.n_q * D * w.n_win * w.num_heads
+    elt = 2 if w.dtype == "bf16" else 4
+    return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_compress=ms_compress,
+                ms_attend=ms_attend, ms_dense=ms_dense, attn_flop=attn_flop,
+                dense_flop=dense_flop,
+                compact_bytes=4.0 * kept * D * elt,
+                kept_frac_hist=(kept / w.num_heads / w.tokens_per_frame - w.cur_frames)
+                / w.hist_frames)
+
+
+def cpu_baseline(w, inp, rows_sample):
+    """The oracle as it stands, timed on this host: full scoring, selection
+    and compaction, attention on a seeded sample of query rows, extrapolated
+    linearly in rows to the whole query block."""
+    from oracle import forcing_kv as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    c = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                   w.tokens_per_frame, w.hist_frames, w.cur_frames, w.query_stride)
+    t1 = time.perf_counter()
+    rows = np.sort(np.random.default_rng(0).choice(w.n_q, rows_sample, replace=False))
+    O.attend(inp.q, c["k_c"], c["v_c"], c["tok_off"], rows=rows)
+    t2 = time.perf_counter()
+    t_layer = (t1 - t0) + (t2 - t1) * (w.n_q / rows_sample)
+    return {"value": w.n_q / t_layer, "unit": "query tok/s per layer", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{w.name}: full compress (score+select+compact, {t1 - t0:.1f} s) + "
+                      f"attention of {rows_sample}/{w.n_q} query rows ({t2 - t1:.1f} s), "
+                      f"attention time scaled by {w.n_q / rows_sample:.2f}; float64 NumPy"}
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import hashlib
+        rec = json.load(open(path)).get(kernel)
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_kv_cache_amd",
+                           "csrc", rec["source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        return rec["bytes_per_launch"] if digest == rec["sha256"] else None
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the path needs no inter-GPU exchange; "
+              f"--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from hybrid_kv_cache_amd import fkv
+    from hybrid_kv_cache_amd import workloads as W
+    fkv.load()
+
+    r = measure(args.workload, args, fkv, torch, W)
+    if args.profile_only:
+        return
+    w = r["w"]
+    value = w.n_q / (r["ms_step"] * 1e-3)
+    attn_tflops = r["attn_flop"] / (r["ms_attend"] * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query tok/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded drift-plus-Gaussian q/k/v, no model weights)",
+        "config": {"workload": w.name, "heads": w.num_heads, "head_dim": w.head_dim,
+                   "tokens_per_frame": w.tokens_per_frame, "hist_frames": w.hist_frames,
+                   "cur_frames": w.cur_frames, "query_tokens": w.n_q, "budget_m": w.budget_m,
+                   "query_stride": w.query_stride, "layer_copies": args.copies},
+        "roofline": {"bound": "mfma", "kernel": "attend_bf16 (fkv_attend)",
+                     "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": attn_tflops / peak, "traffic": traffic_record("attend")},
+        "breakdown_ms": {"compress": r["ms_compress"], "attend": r["ms_attend"],
+                         "attend_dense": r["ms_dense"]},
+        "speedup_vs_full_kv": r["ms_dense"] / r["ms_step"],
+        "attention_speedup_vs_full_kv": r["ms_dense"] / r["ms_attend"],
+        "kept_fraction_of_history_kv": r["kept_frac_hist"],
+        "compact_bytes_per_layer": r["compact_bytes"],
+    }
+    if args.secondary:
+        r2 = measure(args.secondary, args, fkv, torch, W)
+        w2 = r2["w"]
+        line["secondary"] = {
+            "workload": w2.name, "value": w2.n_q / (r2["ms_step"] * 1e-3),
+            "unit": "query tok/s per layer", "ms_per_step": r2["ms_step"],
+            "breakdown_ms": {"compress": r2["ms_compress"], "attend": r2["ms_attend"],
+                             "attend_dense": r2["ms_dense"]},
+            "attend_tflops": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12,
+            "attend_frac_of_peak": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12 / peak,
+            "speedup_vs_full_kv": r2["ms_dense"] / r2["ms_step"],
+            "attention_speedup_vs_full_kv": r2["ms_dense"] / r2["ms_attend"],
+        }
+        del r2
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["inp"], rows_sample=max(1, w.n_q // 4))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

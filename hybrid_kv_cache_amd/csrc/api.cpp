@@ -1,0 +1,318 @@
+// C ABI of libfkv.so (declared in include/fkv.h): argument checks, the
+// data-independent plan (kept counts, offsets, workspace layout) and the
+// launch sequence of the compression and attention kernels.
+//
+// The plan follows the method's split of heads (Forcing-KV, tomesphere page,
+// Abstract; ai-feeds summary, 方法 › 关键模块 2 and 3): a static head keeps
+// the frames its mask marks, a dynamic head keeps min(m, F_h) frames, so every
+// offset is known on the host before any data is read and no call needs a
+// device-to-host copy.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fkv.h"
+#include "fkv_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fkv_status_t fail(fkv_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fkv_status_t ok() {
+  g_last_error.clear();
+  return FKV_OK;
+}
+
+int elt_bytes(int32_t dtype) { return dtype == FKV_BF16 ? 2 : 4; }
+
+float log2e_scale(const fkv_desc_t &d) {
+  const float scale = d.scale != 0.f ? d.scale : 1.0f / std::sqrt((float)d.head_dim);
+  return scale * 1.4426950408889634f;
+}
+
+fkv_status_t check_desc(const fkv_desc_t *d) {
+  if (!d) return fail(FKV_ERR_NULL, "desc is NULL");
+  if (d->dtype != FKV_BF16 && d->dtype != FKV_F32)
+    return fail(FKV_ERR_DTYPE, "dtype %d is neither FKV_BF16 nor FKV_F32", d->dtype);
+  if (d->dtype == FKV_BF16 && d->head_dim != 128)
+    return fail(FKV_ERR_DTYPE, "bf16 needs head_dim 128 (got %d)", d->head_dim);
+  if (d->dtype == FKV_F32 && d->head_dim != 64 && d->head_dim != 128)
+    return fail(FKV_ERR_DTYPE, "fp32 needs head_dim 64 or 128 (got %d)", d->head_dim);
+  if (d->num_heads < 1 || d->num_heads > fkv::kMaxHeads)
+    return fail(FKV_ERR_SHAPE, "num_heads %d outside [1, %d]", d->num_heads, fkv::kMaxHeads);
+  if (d->hist_frames < 0 || d->hist_frames > fkv::kMaxHistFrames)
+    return fail(FKV_ERR_SHAPE, "hist_frames %d outside [0, %d]", d->hist_frames,
+                fkv::kMaxHistFrames);
+  if (d->cur_frames < 1 || d->cur_frames > fkv::kMaxCurFrames)
+    return fail(FKV_ERR_SHAPE, "cur_frames %d outside [1, %d]", d->cur_frames, fkv::kMaxCurFrames);
+  if (d->tokens_per_frame < 1)
+    return fail(FKV_ERR_SHAPE, "tokens_per_frame %d < 1", d->tokens_per_frame);
+  if (d->query_stride < 1) return fail(FKV_ERR_SHAPE, "query_stride %d < 1", d->query_stride);
+  if (!std::isfinite(d->scale) || d->scale < 0.f)
+    return fail(FKV_ERR_SHAPE, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  const int64_t n_win = (int64_t)(d->hist_frames + d->cur_frames) * d->tokens_per_frame;
+  if (n_win >= (int64_t)1 << 31) return fail(FKV_ERR_SHAPE, "window of %lld tokens too long",
+                                            (long long)n_win);
+  return FKV_OK;
+}
+
+struct Plan {
+  int H, D, T, Fh, Fc, Ft, s, n_q, n_win, n_s, m_eff, n_dyn;
+  int dyn_index[fkv::kMaxHeads];
+  int dyn_heads[fkv::kMaxHeads];
+  uint64_t static_bits[fkv::kMaxHeads];
+  int32_t seg_off[fkv::kMaxHeads + 1];
+  int32_t slot_off[fkv::kMaxHeads + 1];
+  int64_t tok_off[fkv::kMaxHeads + 1];
+  size_t ws_lse_off, ws_slot_off, ws_bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+fkv_status_t make_plan(const fkv_desc_t *d, const uint8_t *role, const uint8_t *mask,
+                       int32_t budget_m, Plan *p) {
+  fkv_status_t st = check_desc(d);
+  if (st != FKV_OK) return st;
+  if (!role) return fail(FKV_ERR_NULL, "head_role is NULL");
+  if (budget_m < 0) return fail(FKV_ERR_BUDGET, "budget_m %d < 0", budget_m);
+  p->H = d->num_heads;
+  p->D = d->head_dim;
+  p->T = d->tokens_per_frame;
+  p->Fh = d->hist_frames;
+  p->Fc = d->cur_frames;
+  p->Ft = p->Fh + p->Fc;
+  p->s = d->query_stride;
+  p->n_q = p->Fc * p->T;
+  p->n_win = p->Ft * p->T;
+  p->n_s = (p->n_q + p->s - 1) / p->s;
+  p->m_eff = budget_m < p->Fh ? budget_m : p->Fh;
+  p->n_dyn = 0;
+  bool any_static = false;
+  for (int h = 0; h < p->H; ++h) {
+    if (role[h] != FKV_STATIC && role[h] != FKV_DYNAMIC)
+      return fail(FKV_ERR_SHAPE, "head_role[%d] = %d is neither static (0) nor dynamic (1)", h,
+                  role[h]);
+    any_static |= role[h] == FKV_STATIC;
+  }
+  if (any_static && p->Fh > 0 && !mask)
+    return fail(FKV_ERR_NULL, "static_keep_mask is NULL but static heads exist");
+  p->seg_off[0] = 0;
+  p->slot_off[0] = 0;
+  p->tok_off[0] = 0;
+  for (int h = 0; h < p->H; ++h) {
+    int kept;
+    p->static_bits[h] = 0;
+    if (role[h] == FKV_DYNAMIC) {
+      p->dyn_index[h] = p->n_dyn;
+      p->dyn_heads[p->n_dyn++] = h;
+      kept = p->m_eff;
+    } else {
+      p->dyn_index[h] = -1;
+      uint64_t bits = 0;
+      for (int f = 0; f < p->Fh; ++f)
+        if (mask[(size_t)h * p->Fh + f]) bits |= 1ull << f;
+      p->static_bits[h] = bits;
+      kept = __builtin_popcountll(bits);
+    }
+    p->seg_off[h + 1] = p->seg_off[h] + kept;
+    p->slot_off[h + 1] = p->slot_off[h] + kept + p->Fc;
+    p->tok_off[h + 1] = p->tok_off[h] + (int64_t)(kept + p->Fc) * p->T;
+  }
+  for (int h = p->n_dyn; h < fkv::kMaxHeads; ++h) p->dyn_heads[h] = 0;
+  for (int h = p->H; h < fkv::kMaxHeads; ++h) {
+    p->dyn_index[h] = -1;
+    p->static_bits[h] = 0;
+  }
+  for (int h = p->H + 1; h <= fkv::kMaxHeads; ++h) {
+    p->seg_off[h] = p->seg_off[p->H];
+    p->slot_off[h] = p->slot_off[p->H];
+    p->tok_off[h] = p->tok_off[p->H];
+  }
+  const bool score = p->n_dyn > 0 && p->Fh > 0;
+  const size_t lse_bytes = score ? (size_t)p->n_dyn * p->n_s * p->Ft * sizeof(float) : 0;
+  p->ws_lse_off = 0;
+  p->ws_slot_off = align256(lse_bytes);
+  p->ws_bytes = p->ws_slot_off + align256((size_t)p->slot_off[p->H] * sizeof(fkv::CopySlot));
+  return FKV_OK;
+}
+
+fkv_status_t hip_fail(hipError_t e, const char *what) {
+  return fail(FKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, const void *v,
+                           const int64_t *tok_off, void *out, void *stream) {
+  fkv::AttendArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.tok_off = tok_off;
+  a.kv_row_stride = (int64_t)d->num_heads * d->head_dim;
+  a.dense_len = (d->hist_frames + d->cur_frames) * d->tokens_per_frame;
+  a.n_q = d->cur_frames * d->tokens_per_frame;
+  a.H = d->num_heads;
+  a.D = d->head_dim;
+  a.c = log2e_scale(*d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = d->dtype == FKV_BF16 ? fkv::launch_attend_bf16(a, s) : fkv::launch_attend_f32(a, s);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fkv_status_t fkv_plan(const fkv_desc_t *desc, const uint8_t *head_role,
+                      const uint8_t *static_keep_mask, int32_t budget_m, int64_t *kept_tokens,
+                      size_t *workspace_bytes) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (kept_tokens) *kept_tokens = p.tok_off[p.H];
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                          const void *v_cache, const uint8_t *head_role,
+                          const uint8_t *static_keep_mask, int32_t budget_m, const fkv_ckv_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
+  if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
+    return fail(FKV_ERR_NULL, "a compressed-cache buffer (k, v, tok_off, seg_idx, seg_off) is NULL");
+  if (out->cap_tokens < p.tok_off[p.H])
+    return fail(FKV_ERR_CAPACITY, "cap_tokens %lld < %lld rows needed",
+                (long long)out->cap_tokens, (long long)p.tok_off[p.H]);
+  if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
+    return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  float *lse = reinterpret_cast<float *>(ws + p.ws_lse_off);
+  fkv::CopySlot *slots = reinterpret_cast<fkv::CopySlot *>(ws + p.ws_slot_off);
+  const float c = log2e_scale(*desc);
+
+  // 1. dynamic-head scoring: per (sampled query, frame) log-sum-exp
+  if (p.n_dyn > 0 && p.Fh > 0) {
+    fkv::ScoreArgs sa;
+    sa.q = q;
+    sa.k = k_cache;
+    sa.lse = lse;
+    sa.H = p.H;
+    sa.D = p.D;
+    sa.T = p.T;
+    sa.F_tot = p.Ft;
+    sa.n_s = p.n_s;
+    sa.stride = p.s;
+    sa.n_dyn = p.n_dyn;
+    sa.c = c;
+    std::memcpy(sa.dyn_heads, p.dyn_heads, sizeof(sa.dyn_heads));
+    hipError_t e = desc->dtype == FKV_BF16 ? fkv::launch_score_bf16(sa, s)
+                                           : fkv::launch_score_f32(sa, s);
+    if (e != hipSuccess) return hip_fail(e, "scoring kernel launch");
+  }
+  // 2. selection, offsets and compaction slots
+  {
+    fkv::SelectArgs sa;
+    sa.lse = (p.n_dyn > 0 && p.Fh > 0) ? lse : nullptr;
+    sa.seg_idx = out->seg_idx;
+    sa.seg_off = out->seg_off;
+    sa.tok_off = out->tok_off;
+    sa.seg_score = p.Fh > 0 ? out->seg_score : nullptr;
+    sa.slots = slots;
+    sa.H = p.H;
+    sa.T = p.T;
+    sa.F_h = p.Fh;
+    sa.F_c = p.Fc;
+    sa.F_tot = p.Ft;
+    sa.n_s = p.n_s;
+    sa.m_eff = p.m_eff;
+    for (int h = 0; h < fkv::kMaxHeads; ++h) {
+      // Without history there is nothing to score: every head is handled as
+      // static with an empty mask.
+      sa.dyn_index[h] = p.Fh > 0 ? p.dyn_index[h] : -1;
+      sa.static_bits[h] = p.static_bits[h];
+    }
+    std::memcpy(sa.seg_off_h, p.seg_off, sizeof(sa.seg_off_h));
+    std::memcpy(sa.slot_off_h, p.slot_off, sizeof(sa.slot_off_h));
+    std::memcpy(sa.tok_off_h, p.tok_off, sizeof(sa.tok_off_h));
+    hipError_t e = fkv::launch_select(sa, s);
+    if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
+  }
+  // 3. compaction
+  {
+    fkv::CompactArgs ca;
+    const int eb = elt_bytes(desc->dtype);
+    ca.slots = slots;
+    ca.k = reinterpret_cast<const char *>(k_cache);
+    ca.v = reinterpret_cast<const char *>(v_cache);
+    ca.k_out = reinterpret_cast<char *>(out->k);
+    ca.v_out = reinterpret_cast<char *>(out->v);
+    ca.src_row_bytes = (int64_t)p.H * p.D * eb;
+    ca.row_bytes = p.D * eb;
+    ca.head_bytes = p.D * eb;
+    ca.T = p.T;
+    ca.chunks = (p.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
+    hipError_t e = fkv::launch_compact(ca, p.slot_off[p.H], s);
+    if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
+  }
+  return ok();
+}
+
+fkv_status_t fkv_attend(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv, void *out,
+                        void *stream) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");
+  if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
+    return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  return attend_common(desc, q, ckv->k, ckv->v, ckv->tok_off, out, stream);
+}
+
+fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                              const void *v_cache, void *out, void *stream) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(FKV_ERR_NULL, "q, k_cache, v_cache or out is NULL");
+  return attend_common(desc, q, k_cache, v_cache, nullptr, out, stream);
+}
+
+const char *fkv_status_str(fkv_status_t status) {
+  switch (status) {
+    case FKV_OK: return "ok";
+    case FKV_ERR_NULL: return "null pointer";
+    case FKV_ERR_SHAPE: return "bad shape";
+    case FKV_ERR_DTYPE: return "unsupported dtype / head dim";
+    case FKV_ERR_BUDGET: return "negative budget";
+    case FKV_ERR_CAPACITY: return "compressed cache too small";
+    case FKV_ERR_WORKSPACE: return "workspace too small";
+    case FKV_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *fkv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

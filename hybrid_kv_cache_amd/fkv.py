@@ -1,0 +1,197 @@
+"""ctypes binding of libfkv.so (C ABI in include/fkv.h).
+
+Argument marshalling only: torch tensors become device pointers and the
+current torch stream becomes the hipStream_t; every step of the path runs in
+the library's HIP kernels.  Loading fails loudly when the library has not
+been built (``python -m hybrid_kv_cache_amd.build``); there is no fallback.
+
+Names mirror the C ABI: fkv_plan, fkv_compress, fkv_attend, fkv_attend_dense,
+fkv_status_str, fkv_last_error.  ``CompressedKV`` allocates the ragged cache
+and workspace for one layer with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfkv.so")
+
+FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
+    FKV_ERR_CAPACITY, FKV_ERR_WORKSPACE, FKV_ERR_HIP = range(8)
+FKV_BF16, FKV_F32 = 0, 1
+FKV_STATIC, FKV_DYNAMIC = 0, 1
+
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_attend", "fkv_attend_dense",
+            "fkv_status_str", "fkv_last_error")
+
+
+class FkvDesc(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("hist_frames", ctypes.c_int32),
+                ("cur_frames", ctypes.c_int32), ("query_stride", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class FkvCkv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("tok_off", ctypes.c_void_p), ("seg_idx", ctypes.c_void_p),
+                ("seg_off", ctypes.c_void_p), ("seg_score", ctypes.c_void_p),
+                ("cap_tokens", ctypes.c_int64)]
+
+
+class FkvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"fkv status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfkv.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m hybrid_kv_cache_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.fkv_plan.argtypes = [ctypes.POINTER(FkvDesc), P, P, I32, ctypes.POINTER(I64),
+                             ctypes.POINTER(SZ)]
+    lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
+                                 ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P]
+    lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P]
+    for name in ("fkv_plan", "fkv_compress", "fkv_attend", "fkv_attend_dense"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fkv_status_str.argtypes = [ctypes.c_int]
+    lib.fkv_status_str.restype = ctypes.c_char_p
+    lib.fkv_last_error.argtypes = []
+    lib.fkv_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != FKV_OK:
+        lib = load()
+        raise FkvError(status, f"{lib.fkv_status_str(status).decode()}: "
+                               f"{lib.fkv_last_error().decode()}")
+
+
+def make_desc(num_heads, head_dim, tokens_per_frame, hist_frames, cur_frames,
+              query_stride, dtype="bf16", scale=0.0) -> FkvDesc:
+    return FkvDesc(num_heads, head_dim, tokens_per_frame, hist_frames, cur_frames,
+                   query_stride, float(scale), FKV_BF16 if dtype == "bf16" else FKV_F32)
+
+
+def desc_for(w, scale: float = 0.0) -> FkvDesc:
+    """Descriptor of a hybrid_kv_cache_amd.workloads.Workload."""
+    return make_desc(w.num_heads, w.head_dim, w.tokens_per_frame, w.hist_frames,
+                     w.cur_frames, w.query_stride, w.dtype, scale)
+
+
+def _host_u8(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fkv_plan(desc: FkvDesc, head_role, static_keep_mask, budget_m: int):
+    """Returns (kept_tokens, workspace_bytes)."""
+    lib = load()
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    kept = ctypes.c_int64(0)
+    ws = ctypes.c_size_t(0)
+    _check(lib.fkv_plan(ctypes.byref(desc), role.ctypes.data, mask.ctypes.data if mask.size else None,
+                        int(budget_m), ctypes.byref(kept), ctypes.byref(ws)))
+    return kept.value, ws.value
+
+
+class CompressedKV:
+    """Device buffers of one layer's compressed cache, allocated with torch."""
+
+    def __init__(self, desc: FkvDesc, head_role, static_keep_mask, budget_m: int,
+                 device="cuda", with_scores: bool = True):
+        import torch
+        self.kept_tokens, self.workspace_bytes = fkv_plan(desc, head_role, static_keep_mask,
+                                                          budget_m)
+        H, D, Fh = desc.num_heads, desc.head_dim, desc.hist_frames
+        dt = torch.bfloat16 if desc.dtype == FKV_BF16 else torch.float32
+        self.k = torch.empty((max(self.kept_tokens, 1), D), dtype=dt, device=device)
+        self.v = torch.empty((max(self.kept_tokens, 1), D), dtype=dt, device=device)
+        self.tok_off = torch.empty(H + 1, dtype=torch.int64, device=device)
+        self.seg_idx = torch.empty(max(H * Fh, 1), dtype=torch.int32, device=device)
+        self.seg_off = torch.empty(H + 1, dtype=torch.int32, device=device)
+        self.seg_score = (torch.empty(max(H * Fh, 1), dtype=torch.float32, device=device)
+                          if with_scores else None)
+        self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
+                                     device=device)
+
+    def struct(self) -> FkvCkv:
+        return FkvCkv(_ptr(self.k), _ptr(self.v), _ptr(self.tok_off), _ptr(self.seg_idx),
+                      _ptr(self.seg_off), _ptr(self.seg_score), self.kept_tokens)
+
+
+def fkv_compress(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask,
+                 budget_m: int, ckv: CompressedKV, stream=None) -> None:
+    lib = load()
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    out = ckv.struct()
+    _check(lib.fkv_compress(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                            role.ctypes.data, mask.ctypes.data if mask.size else None,
+                            int(budget_m), ctypes.byref(out), _ptr(ckv.workspace),
+                            ckv.workspace_bytes, _stream(stream)))
+
+
+def fkv_attend(desc: FkvDesc, q, ckv: CompressedKV, out, stream=None) -> None:
+    lib = load()
+    s = ckv.struct()
+    _check(lib.fkv_attend(ctypes.byref(desc), _ptr(q), ctypes.byref(s), _ptr(out),
+                          _stream(stream)))
+
+
+def fkv_attend_dense(desc: FkvDesc, q, k_cache, v_cache, out, stream=None) -> None:
+    lib = load()
+    _check(lib.fkv_attend_dense(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(out), _stream(stream)))
+
+
+def fkv_status_str(status: int) -> str:
+    return load().fkv_status_str(status).decode()
+
+
+def fkv_last_error() -> str:
+    return load().fkv_last_error().decode()
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """Host array (float32 values or bf16 bit patterns as uint16) -> torch tensor."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    """torch tensor -> host array (bf16 returned as uint16 bit patterns)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,143 @@
+/*
+ * fkv.h -- C ABI of libfkv.so: the per-layer hot path of Forcing-KV hybrid
+ * head-wise KV-cache compression on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes (pages on the method):
+ *   [S] "Forcing-KV：面向高效自回归视频扩散模型的混合KV缓存压缩" (ai-feeds.com
+ *       summary of arXiv 2605.09681), section 方法 (Method): 输入与整体流程,
+ *       关键模块 2 (static structural pruning), 关键模块 3 (dynamic similarity
+ *       pruning), 输出与工程收益 (the compressed KV replaces the cache in the
+ *       layer's attention); section 行业影响 › 与现有产品/工作流的接口 (a
+ *       plug-in applied per attention layer at every denoising step, head
+ *       labels produced offline once).
+ *   [A] "Forcing-KV: Hybrid KV Cache Compression for Efficient Autoregressive
+ *       Video Diffusion Models" (tomesphere.com), Abstract.
+ *
+ * Shapes and layouts (all tensors contiguous, row-major, in device memory
+ * owned by the caller; T = tokens per latent frame, F_h history frames, F_c
+ * current-chunk frames, H heads, D head dim):
+ *   q        [Nq,    H, D]   Nq    = F_c * T        current chunk's queries
+ *   k_cache  [N_win, H, D]   N_win = (F_h + F_c) * T
+ *   v_cache  [N_win, H, D]   frames oldest first; the current chunk is last
+ *   out      [Nq,    H, D]   same dtype as q
+ * Element type: bf16 with D = 128, or fp32 with D = 64 or 128.
+ * Limits: 1 <= H <= 64, 0 <= F_h <= 64, 1 <= F_c <= 8, 1 <= T, s >= 1,
+ *         N_win < 2^31; element offsets are computed in 64 bits.
+ *
+ * Threading and streams: calls are stateless apart from the thread-local
+ * error string; every device operation is enqueued on the given stream
+ * (a hipStream_t passed as void*, NULL = the default stream) and no call
+ * waits for the device.  The library allocates no device memory.
+ *
+ * Errors: argument errors are detected on the host before any HIP call and
+ * returned as a status; a failed kernel launch returns FKV_ERR_HIP.  Faults
+ * inside kernels surface at the caller's next synchronisation.  The text of
+ * the last error on the calling thread is returned by fkv_last_error().
+ */
+#ifndef FKV_H
+#define FKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FKV_OK = 0,
+  FKV_ERR_NULL = 1,       /* a required pointer is NULL                        */
+  FKV_ERR_SHAPE = 2,      /* a size is out of range or inconsistent            */
+  FKV_ERR_DTYPE = 3,      /* unsupported element type / head dim combination   */
+  FKV_ERR_BUDGET = 4,     /* budget_m < 0                                      */
+  FKV_ERR_CAPACITY = 5,   /* compressed buffers too small for the kept rows    */
+  FKV_ERR_WORKSPACE = 6,  /* workspace smaller than fkv_plan's figure          */
+  FKV_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed        */
+} fkv_status_t;
+
+typedef enum { FKV_BF16 = 0, FKV_F32 = 1 } fkv_dtype_t;
+
+/* Head roles, produced by offline profiling ([S] 关键模块 1). */
+typedef enum { FKV_STATIC = 0, FKV_DYNAMIC = 1 } fkv_role_t;
+
+/* Problem description shared by every call. */
+typedef struct fkv_desc {
+  int32_t num_heads;        /* H                                              */
+  int32_t head_dim;         /* D                                              */
+  int32_t tokens_per_frame; /* T                                              */
+  int32_t hist_frames;      /* F_h: history frames in the window              */
+  int32_t cur_frames;       /* F_c: frames of the current chunk (queries)     */
+  int32_t query_stride;     /* s: dynamic scoring uses queries 0, s, 2s, ...  */
+  float scale;              /* logit scale; 0 selects 1/sqrt(D)               */
+  int32_t dtype;            /* fkv_dtype_t of q, k_cache, v_cache, ckv, out   */
+} fkv_desc_t;
+
+/* The compressed cache of one layer ([S] 输出与工程收益): ragged, head-major.
+ * Head h owns rows [tok_off[h], tok_off[h+1]) of k and v: the T rows of each
+ * kept history frame in ascending frame order, then the T rows of each
+ * current-chunk frame.  All pointers are caller-owned device memory. */
+typedef struct fkv_ckv {
+  void *k;             /* [cap_tokens, D] dtype                                */
+  void *v;             /* [cap_tokens, D] dtype                                */
+  int64_t *tok_off;    /* [H + 1]                                              */
+  int32_t *seg_idx;    /* [H * F_h] kept history frames; head h's are
+                          seg_idx[seg_off[h] .. seg_off[h+1]), ascending       */
+  int32_t *seg_off;    /* [H + 1]                                              */
+  float *seg_score;    /* [H * F_h] or NULL: score of every history frame of
+                          every head (mean softmax mass); NaN for static heads */
+  int64_t cap_tokens;  /* rows available in k and v                            */
+} fkv_ckv_t;
+
+/* Host-only planning.  The kept counts depend only on the roles, the static
+ * mask and the budget, so the compressed size is known before any data is
+ * read.  head_role [H] and static_keep_mask [H * F_h] (row-major; rows of
+ * dynamic heads ignored) are host arrays.  Writes the rows the compressed
+ * cache needs (tok_off[H]) to *kept_tokens and the workspace bytes
+ * fkv_compress needs to *workspace_bytes.  Either output pointer may be NULL.
+ * A budget above F_h keeps every history frame of a dynamic head. */
+fkv_status_t fkv_plan(const fkv_desc_t *desc, const uint8_t *head_role,
+                      const uint8_t *static_keep_mask, int32_t budget_m,
+                      int64_t *kept_tokens, size_t *workspace_bytes);
+
+/* Compression of one layer ([S] 关键模块 2 and 3; [A]):
+ *  - static heads keep the history frames their mask row marks;
+ *  - dynamic heads score each history frame by the softmax attention mass
+ *    it receives (softmax over the whole window, current chunk included,
+ *    scale * q.k logits) averaged over the strided query sample, and keep
+ *    the min(budget_m, F_h) best frames, ties to the lower frame index;
+ *  - the kept frames and the current chunk are copied into out->k / out->v
+ *    and the offsets written.
+ * q, k_cache, v_cache: device tensors as above.  head_role, static_keep_mask:
+ * host arrays as in fkv_plan.  workspace: device memory of at least the
+ * bytes fkv_plan reports (NULL allowed when that figure is 0); its contents
+ * on entry do not matter.  out->seg_score may be NULL. */
+fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                          const void *v_cache, const uint8_t *head_role,
+                          const uint8_t *static_keep_mask, int32_t budget_m,
+                          const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Attention of the whole query block over the compressed cache ([S]
+ * 输出与工程收益): out[i, h] = sum_j softmax_j(scale * q[i,h].k_j) v_j over
+ * head h's compressed rows, non-causal, fp32 accumulation, result rounded to
+ * the element type.  ckv must hold what fkv_compress wrote (only k, v and
+ * tok_off are read). */
+fkv_status_t fkv_attend(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
+                        void *out, void *stream);
+
+/* Full-KV baseline: the same attention kernel over the whole uncompressed
+ * window (every query sees all N_win keys of its head). */
+fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                              const void *v_cache, void *out, void *stream);
+
+/* Static text for a status code. */
+const char *fkv_status_str(fkv_status_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *fkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FKV_H */

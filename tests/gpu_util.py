@@ -1,0 +1,118 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare with the CPU oracle to the stated bar."""
+import sys
+
+import numpy as np
+
+from hybrid_kv_cache_amd import fkv
+from oracle import forcing_kv as O
+
+# Output tolerances: bf16 inputs with fp32 accumulation / fp32 inputs.
+BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3
+F32_MAX_ABS = 1e-4
+
+
+def announce(msg: str) -> None:
+    """Name the case on the real stderr before a GPU step (survives capture)."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def require_gpu():
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fkv.load()  # fails loudly when the library is missing
+
+
+def upload(inp):
+    return fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v)
+
+
+def run_compress(w, inp, budget_m=None, mask=None, role=None, q=None, k=None, v=None):
+    """Compress one layer on the GPU; returns (desc, ckv, host results)."""
+    import torch
+    budget_m = w.budget_m if budget_m is None else budget_m
+    mask = inp.static_keep_mask if mask is None else mask
+    role = inp.head_role if role is None else role
+    if q is None:
+        q, k, v = upload(inp)
+    desc = fkv.desc_for(w)
+    ckv = fkv.CompressedKV(desc, role, mask, budget_m)
+    announce(f"fkv_compress {w.name} layer={inp.layer} H={w.num_heads} T={w.tokens_per_frame} "
+             f"Fh={w.hist_frames} m={budget_m}")
+    fkv.fkv_compress(desc, q, k, v, role, mask, budget_m, ckv)
+    torch.cuda.synchronize()
+    H, Fh = w.num_heads, w.hist_frames
+    res = dict(
+        seg_off=fkv.to_host(ckv.seg_off),
+        tok_off=fkv.to_host(ckv.tok_off),
+        seg_idx=fkv.to_host(ckv.seg_idx)[: max(H * Fh, 0)],
+        seg_score=fkv.to_host(ckv.seg_score)[: H * Fh].reshape(H, Fh),
+    )
+    return desc, ckv, (q, k, v), res
+
+
+def run_attend(desc, q, ckv, n_q, H, D, dtype):
+    import torch
+    out = torch.empty((n_q, H, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device="cuda")
+    announce(f"fkv_attend Nq={n_q} H={H} D={D} kept={ckv.kept_tokens}")
+    fkv.fkv_attend(desc, q, ckv, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_attend_dense(desc, q, k, v, n_q, H, D, dtype):
+    import torch
+    out = torch.empty((n_q, H, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device="cuda")
+    announce(f"fkv_attend_dense Nq={n_q} H={H} D={D}")
+    fkv.fkv_attend_dense(desc, q, k, v, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def host_f64(t) -> np.ndarray:
+    return O.as_f64(fkv.to_host(t))
+
+
+def check_selection(w, res, oracle_scores, role, mask, budget_m):
+    """Kept frames per head: exact outside the cutoff tie band; offsets exact.
+    Returns the list of GPU kept frames per head."""
+    H, Fh, T, Fc = w.num_heads, w.hist_frames, w.tokens_per_frame, w.cur_frames
+    seg_off, seg_idx = res["seg_off"], res["seg_idx"]
+    gpu_kept = [np.array(seg_idx[seg_off[h]:seg_off[h + 1]], dtype=np.int64) for h in range(H)]
+    for h in range(H):
+        g = list(gpu_kept[h])
+        assert g == sorted(set(g)), f"head {h}: seg_idx not strictly ascending: {g}"
+        if role[h] == O.DYNAMIC:
+            assert O.kept_set_valid(g, oracle_scores[h], budget_m), \
+                f"head {h}: kept {g} vs oracle scores {oracle_scores[h]}"
+        else:
+            assert g == list(np.flatnonzero(mask[h])), f"static head {h}: {g}"
+    # offsets follow from the kept counts exactly
+    _, seg_off_o, tok_off_o = O.offsets(gpu_kept, T, Fc)
+    np.testing.assert_array_equal(seg_off, seg_off_o)
+    np.testing.assert_array_equal(res["tok_off"], tok_off_o)
+    return gpu_kept
+
+
+def check_scores(res, oracle_scores, role, rtol=1e-3):
+    s = res["seg_score"]
+    for h in range(len(role)):
+        if role[h] == O.DYNAMIC:
+            np.testing.assert_allclose(s[h], oracle_scores[h], rtol=rtol, atol=1e-7)
+        else:
+            assert np.isnan(s[h]).all()
+
+
+def check_output(got, ref, dtype):
+    err = np.abs(got - ref)
+    if dtype == "bf16":
+        assert err.max() <= BF16_MAX_ABS, f"max abs err {err.max()}"
+        assert err.mean() <= BF16_MEAN_ABS, f"mean abs err {err.mean()}"
+    else:
+        assert err.max() <= F32_MAX_ABS, f"max abs err {err.max()}"
+    return float(err.max()), float(err.mean())

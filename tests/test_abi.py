@@ -1,0 +1,175 @@
+"""C-ABI contract of libfkv.so on the host (no GPU needed).
+
+Loads the built library, checks that every function include/fkv.h declares
+is exported, and drives the argument checks and the host-side plan, all of
+which return before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from hybrid_kv_cache_amd import fkv
+from hybrid_kv_cache_amd import workloads as W
+from oracle import forcing_kv as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fkv.LIB_PATH):
+        pytest.fail("libfkv.so is not built: run python -m hybrid_kv_cache_amd.build")
+    return fkv.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(fkv.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(fkv.FkvDesc) == 32
+    assert ctypes.sizeof(fkv.FkvCkv) == 56
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert fkv.fkv_status_str(st)
+    assert fkv.fkv_status_str(99) == "unknown status"
+
+
+def _plan(desc, role, mask, m):
+    lib = fkv.load()
+    kept = ctypes.c_int64(-1)
+    ws = ctypes.c_size_t(0)
+    role = np.ascontiguousarray(role, np.uint8)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    st = lib.fkv_plan(ctypes.byref(desc) if desc is not None else None, role.ctypes.data,
+                      mask.ctypes.data if mask.size else None, m, ctypes.byref(kept),
+                      ctypes.byref(ws))
+    return st, kept.value, ws.value
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_plan_matches_oracle_offsets(lib, name):
+    w = W.WORKLOADS[name]
+    rng = np.random.default_rng(1)
+    role = np.zeros(w.num_heads, np.uint8)
+    role[rng.permutation(w.num_heads)[: w.num_heads - w.num_static]] = 1
+    mask = np.tile(W.chunk_boundary_mask(w.hist_frames), (w.num_heads, 1))
+    st, kept_tokens, ws = _plan(fkv.desc_for(w), role, mask, w.budget_m)
+    assert st == fkv.FKV_OK, fkv.fkv_last_error()
+    kept = O.select_frames(np.zeros((w.num_heads, w.hist_frames)), role, mask, w.budget_m)
+    _, _, tok_off = O.offsets(kept, w.tokens_per_frame, w.cur_frames)
+    assert kept_tokens == tok_off[-1]
+    n_dyn = int(role.sum())
+    assert ws >= n_dyn * w.n_sampled * w.frames * 4
+
+
+def test_plan_examples(lib):
+    # the 480P layer: 6 static heads keep 12 frames, 6 dynamic keep 13
+    d = fkv.make_desc(12, 128, 1560, 18, 3, 16)
+    role = np.array([0] * 6 + [1] * 6, np.uint8)
+    mask = np.tile(W.chunk_boundary_mask(18), (12, 1))
+    st, kept, _ = _plan(d, role, mask, 13)
+    assert st == 0 and kept == 6 * 15 * 1560 + 6 * 16 * 1560 == 290160
+    # budget above the history keeps everything
+    st, kept, _ = _plan(d, np.ones(12, np.uint8), mask, 100)
+    assert st == 0 and kept == 12 * 21 * 1560
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, fkv.FKV_ERR_DTYPE),
+    ("head_dim", 64, fkv.FKV_ERR_DTYPE),        # bf16 needs 128
+    ("num_heads", 0, fkv.FKV_ERR_SHAPE),
+    ("num_heads", 65, fkv.FKV_ERR_SHAPE),
+    ("hist_frames", -1, fkv.FKV_ERR_SHAPE),
+    ("hist_frames", 65, fkv.FKV_ERR_SHAPE),
+    ("cur_frames", 0, fkv.FKV_ERR_SHAPE),
+    ("tokens_per_frame", 0, fkv.FKV_ERR_SHAPE),
+    ("query_stride", 0, fkv.FKV_ERR_SHAPE),
+    ("scale", -1.0, fkv.FKV_ERR_SHAPE),
+])
+def test_plan_rejects_bad_desc(lib, field, value, status):
+    d = fkv.make_desc(4, 128, 16, 6, 3, 4)
+    setattr(d, field, value)
+    st, _, _ = _plan(d, np.ones(max(d.num_heads, 1), np.uint8)[: max(d.num_heads, 1)],
+                     np.ones((max(d.num_heads, 1), max(d.hist_frames, 0)), np.uint8), 2)
+    assert st == status
+    assert fkv.fkv_last_error()
+
+
+def test_plan_null_and_budget(lib):
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    st, _, _ = _plan(None, np.ones(2, np.uint8), np.ones((2, 4), np.uint8), 2)
+    assert st == fkv.FKV_ERR_NULL
+    st, _, _ = _plan(d, np.ones(2, np.uint8), np.ones((2, 4), np.uint8), -1)
+    assert st == fkv.FKV_ERR_BUDGET
+    st, _, _ = _plan(d, np.array([1, 2], np.uint8), np.ones((2, 4), np.uint8), 2)
+    assert st == fkv.FKV_ERR_SHAPE
+    # static heads without a mask
+    lib = fkv.load()
+    role = np.zeros(2, np.uint8)
+    st = lib.fkv_plan(ctypes.byref(d), role.ctypes.data, None, 2, None, None)
+    assert st == fkv.FKV_ERR_NULL
+    # all dynamic: the mask may be NULL
+    role = np.ones(2, np.uint8)
+    st = lib.fkv_plan(ctypes.byref(d), role.ctypes.data, None, 2, None, None)
+    assert st == fkv.FKV_OK
+
+
+def _compress_status(d, cap, ws_bytes, null_k=False, null_ws=False):
+    lib = fkv.load()
+    role = np.ones(d.num_heads, np.uint8)
+    mask = np.zeros((d.num_heads, d.hist_frames), np.uint8)
+    fake = 0x1000  # never dereferenced: every check below fails before HIP
+    ckv = fkv.FkvCkv(None if null_k else fake, fake, fake, fake, fake, None, cap)
+    return lib.fkv_compress(ctypes.byref(d), fake, fake, fake, role.ctypes.data,
+                            mask.ctypes.data, 2, ctypes.byref(ckv),
+                            None if null_ws else fake, ws_bytes, None)
+
+
+def test_compress_argument_errors_before_any_hip_call(lib):
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    st, kept, ws = _plan(d, np.ones(2, np.uint8), np.zeros((2, 4), np.uint8), 2)
+    assert st == 0
+    assert _compress_status(d, kept - 1, ws) == fkv.FKV_ERR_CAPACITY
+    assert _compress_status(d, kept, ws - 1) == fkv.FKV_ERR_WORKSPACE
+    assert _compress_status(d, kept, ws, null_ws=True) == fkv.FKV_ERR_WORKSPACE
+    assert _compress_status(d, kept, ws, null_k=True) == fkv.FKV_ERR_NULL
+    assert "cap_tokens" in _capture_error(d, kept - 1, ws)
+
+
+def _capture_error(d, cap, ws):
+    _compress_status(d, cap, ws)
+    return fkv.fkv_last_error()
+
+
+def test_attend_argument_errors(lib):
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    ckv = fkv.FkvCkv(None, None, None, None, None, None, 0)
+    assert lib.fkv_attend(ctypes.byref(d), 0x1000, ctypes.byref(ckv), 0x1000, None) == \
+        fkv.FKV_ERR_NULL
+    assert lib.fkv_attend_dense(ctypes.byref(d), 0x1000, None, 0x1000, 0x1000, None) == \
+        fkv.FKV_ERR_NULL
+    d.dtype = 5
+    assert lib.fkv_attend_dense(ctypes.byref(d), 1, 1, 1, 1, None) == fkv.FKV_ERR_DTYPE

@@ -1,0 +1,139 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, at
+sizes the oracle finishes in seconds: several tiles per head, ragged tails,
+and the degenerate cases of the method."""
+import numpy as np
+import pytest
+
+from hybrid_kv_cache_amd import fkv
+from hybrid_kv_cache_amd import workloads as W
+from oracle import forcing_kv as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.require_gpu()
+
+
+def full_case(w, inp, budget_m=None, mask=None, role=None, check_dense=True):
+    budget_m = w.budget_m if budget_m is None else budget_m
+    mask = inp.static_keep_mask if mask is None else mask
+    role = inp.head_role if role is None else role
+    desc, ckv, (q, k, v), res = G.run_compress(w, inp, budget_m, mask, role)
+    scores = O.segment_scores(inp.q, inp.k, role, w.tokens_per_frame, w.hist_frames,
+                              w.query_stride)
+    G.check_scores(res, scores, role)
+    kept = G.check_selection(w, res, scores, role, mask, budget_m)
+    k_c, v_c, _, _, tok_off = O.compact(inp.k, inp.v, kept, w.tokens_per_frame,
+                                        w.hist_frames, w.cur_frames)
+    n = int(tok_off[-1])
+    assert np.array_equal(fkv.to_host(ckv.k)[:n], k_c), "compacted K differs"
+    assert np.array_equal(fkv.to_host(ckv.v)[:n], v_c), "compacted V differs"
+    out = G.run_attend(desc, q, ckv, w.n_q, w.num_heads, w.head_dim, w.dtype)
+    ref = O.attend(inp.q, k_c, v_c, tok_off)
+    errs = G.check_output(G.host_f64(out), ref, w.dtype)
+    if check_dense:
+        dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype)
+        G.check_output(G.host_f64(dout), O.attend_dense(inp.q, inp.k, inp.v), w.dtype)
+    return desc, ckv, (q, k, v), out, kept, errs
+
+
+def test_tiny_f32_workload():
+    w = W.WORKLOADS["tiny_f32"]
+    full_case(w, W.generate_layer(w))
+
+
+@pytest.mark.parametrize("T,H,Fh,s,m,nst,seed", [
+    (100, 3, 6, 4, 4, 1, 7),      # 300 queries, 900-key window: ragged tiles
+    (37, 5, 8, 3, 5, 2, 8),       # tiny frames, many heads
+    (64, 2, 6, 1, 3, 0, 9),       # every query scored, all dynamic, exact tiles
+    (130, 4, 18, 16, 13, 2, 10),  # 18 history frames as in the video workloads
+])
+def test_small_bf16(T, H, Fh, s, m, nst, seed):
+    w = W.small_workload(tokens_per_frame=T, num_heads=H, hist_frames=Fh, query_stride=s,
+                         budget_m=m, num_static=nst, seed=seed)
+    full_case(w, W.generate_layer(w))
+
+
+def test_small_f32_d128():
+    w = W.small_workload(name="small_f32", dtype="f32", head_dim=128, tokens_per_frame=40,
+                         num_heads=3, hist_frames=5, query_stride=5, budget_m=2, seed=11)
+    full_case(w, W.generate_layer(w))
+
+
+def test_keep_all_equals_dense_bitwise():
+    """Keep-all budgets and all-ones masks: the compressed cache is the whole
+    window in order, so attend and attend_dense run the same arithmetic."""
+    w = W.small_workload(tokens_per_frame=70, num_heads=3, hist_frames=6, budget_m=6, seed=12)
+    inp = W.generate_layer(w)
+    mask = np.ones_like(inp.static_keep_mask)
+    desc, ckv, (q, k, v), out, kept, _ = full_case(w, inp, budget_m=6, mask=mask,
+                                                   check_dense=False)
+    assert all(list(kh) == list(range(6)) for kh in kept)
+    dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype)
+    assert np.array_equal(fkv.to_host(out), fkv.to_host(dout))
+
+
+def test_budget_above_history_keeps_all():
+    w = W.small_workload(tokens_per_frame=20, num_heads=2, hist_frames=4, budget_m=9,
+                         num_static=0, seed=13)
+    _, _, _, _, kept, _ = full_case(w, W.generate_layer(w), budget_m=9)
+    assert all(list(kh) == [0, 1, 2, 3] for kh in kept)
+
+
+def test_zero_budget_and_empty_mask_attend_current_chunk_only():
+    w = W.small_workload(tokens_per_frame=50, num_heads=3, hist_frames=6, budget_m=0, seed=14)
+    inp = W.generate_layer(w)
+    mask = np.zeros_like(inp.static_keep_mask)
+    desc, ckv, (q, k, v), out, kept, _ = full_case(w, inp, budget_m=0, mask=mask,
+                                                   check_dense=False)
+    assert all(len(kh) == 0 for kh in kept)
+    cur = slice(w.hist_frames * w.tokens_per_frame, None)
+    ref = O.attend_dense(inp.q, inp.k[cur], inp.v[cur])
+    G.check_output(G.host_f64(out), ref, w.dtype)
+
+
+def test_zero_queries_tie_break_lowest_frames():
+    """q = 0: every frame receives exactly the same mass, and the kept set of
+    every dynamic head is frames 0..m-1 on both sides."""
+    for dtype, D in (("bf16", 128), ("f32", 64)):
+        w = W.small_workload(name=f"zeroq_{dtype}", dtype=dtype, head_dim=D,
+                             tokens_per_frame=90, num_heads=3, hist_frames=7, budget_m=4,
+                             num_static=1, seed=15)
+        inp = W.generate_layer(w, zero_q=True)
+        desc, ckv, _, res = G.run_compress(w, inp)
+        for h in range(w.num_heads):
+            if inp.head_role[h] == O.DYNAMIC:
+                s = res["seg_score"][h]
+                assert np.all(s == s[0]), s
+                kh = res["seg_idx"][res["seg_off"][h]:res["seg_off"][h + 1]]
+                assert list(kh) == [0, 1, 2, 3]
+
+
+def test_no_history_single_head_single_token_frames():
+    w = W.small_workload(tokens_per_frame=1, num_heads=1, hist_frames=0, cur_frames=3,
+                         budget_m=2, num_static=0, query_stride=1, seed=16)
+    full_case(w, W.generate_layer(w))
+    w = W.small_workload(tokens_per_frame=1, num_heads=1, hist_frames=5, cur_frames=1,
+                         budget_m=2, num_static=0, query_stride=1, seed=17)
+    full_case(w, W.generate_layer(w))
+
+
+def test_max_heads_and_frames():
+    w = W.small_workload(tokens_per_frame=3, num_heads=64, hist_frames=64, cur_frames=8,
+                         budget_m=40, num_static=20, query_stride=2, seed=18)
+    full_case(w, W.generate_layer(w))
+
+
+def test_deterministic_across_runs():
+    w = W.small_workload(tokens_per_frame=100, num_heads=3, hist_frames=6, seed=19)
+    inp = W.generate_layer(w)
+    outs = []
+    for _ in range(2):
+        desc, ckv, (q, k, v), res = G.run_compress(w, inp)
+        out = G.run_attend(desc, q, ckv, w.n_q, w.num_heads, w.head_dim, w.dtype)
+        outs.append((res["seg_score"].copy(), fkv.to_host(ckv.k).copy(), fkv.to_host(out)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b, equal_nan=True) if a.dtype.kind == "f" else np.array_equal(a, b)
