@@ -6,12 +6,16 @@
 // every row of its head's range.
 //
 // bf16 kernel (D = 128): one workgroup = 4 waves x 32 queries of one head.
-// K/V tiles of 64 keys are staged through LDS (double buffered, one barrier
-// per tile, the next tile's global loads in flight during the current
-// tile's math).  Scores S^T = K Q^T and the output O^T = V^T P^T run on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the softmax is the online
-// (running max / running sum) form in base 2 with the logit scale folded
-// into the exponent.
+// K and V tiles of 64 keys are copied row-major from global memory straight
+// into LDS (global_load_lds, double buffered, one barrier per tile, the next
+// tile's copies in flight during the current tile's math).  Scores S^T = K Q^T and the output
+// O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
+// V^T operand comes straight from the row-major tile through transposing LDS
+// reads.  Softmax: online form in base 2 with the logit scale folded into
+// one FMA per score; the running maximum is raised (and the accumulator
+// rescaled) only when a tile's maximum exceeds it by more than 2^8, which
+// leaves the result exact (the final division uses the same reference) and
+// removes the per-tile rescale of the 64 accumulator registers.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
@@ -22,9 +26,8 @@ constexpr int kD = 128;
 constexpr int kKT = 64;      // keys per tile
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
-constexpr int kKBytes = KTileLds<kKT>::kBytes;
-constexpr int kVBytes = VtTileLds::kBytes;
-constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kTileBytes = KvTileLds<kKT>::kBytes;
+constexpr float kLazyRescale = 8.0f;         // log2 of the allowed growth
 
 struct KvView {
   const __bf16 *k;
@@ -51,13 +54,19 @@ __device__ __forceinline__ KvView kv_view(const AttendArgs &a, int h) {
 }
 
 __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  // LDS: two K tiles and two V tiles.  Iteration t reads K(t+1) and V(t)
+  // while K(t+2) and V(t+1) are copied into the other two.
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
+  auto kbuf = [&](int i) { return smem + (i & 1) * kTileBytes; };
+  auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * kTileBytes; };
+  typedef KvTileLds<kKT> Lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int h = blockIdx.y;
   const int qi = blockIdx.x * kBM + wave * 32 + col;
   const KvView kv = kv_view(a, h);
+  const int64_t rs_bytes = kv.rs * 2;
 
   // Q^T fragments (B operand of S^T = K Q^T): query qi, dims 16*st + 8*g ..
   bf16x8 qf[8];
@@ -74,118 +83,179 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m = kNegBig, l = 0.f;
+  const float c = a.c;
 
-  // Staging: K rows (tid>>4) + 16 i, chunk tid&15; V rows 4*(tid>>4) + i,
-  // chunk tid&15 (four consecutive keys per thread, transposed on the way
-  // into LDS).
-  const int sc = tid & 15, sr = tid >> 4;
-  u32x4 kr[4], vr[4];
-  auto load_tile = [&](int t0) {
+  // Staging: wave w fills tile rows 16 w .. 16 w + 15, four rows per
+  // instruction; lane i lands at row 16 w + 4 j + i/16, chunk position i%16,
+  // so it fetches global chunk (i%16) ^ swz(row) of that row.
+  const int lrow = lane >> 4, lpos = lane & 15;
+  int32_t goff[4];   // byte offset of the lane's chunk from the tile's first row
+  int trow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t0 + sr + 16 * i;
-      kr[i] = key < kv.len ? ld16(kv.k + key * kv.rs + sc * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int j = 0; j < 4; ++j) {
+    trow[j] = 16 * wave + 4 * j + lrow;
+    goff[j] = trow[j] * (int32_t)rs_bytes + (int32_t)((lpos ^ Lds::swz(trow[j])) << 4);
+  }
+  auto issue = [&](const __bf16 *src, int it, char *dst) {
+    const int t0 = it * kKT;
+    const char *tb = reinterpret_cast<const char *>(src) + (int64_t)t0 * rs_bytes;
+    if (t0 + kKT <= kv.len) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t0 + 4 * sr + i;
-      vr[i] = key < kv.len ? ld16(kv.v + key * kv.rs + sc * 8) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) load_lds16(tb + goff[j], dst + (16 * wave + 4 * j) * 256);
+    } else {
+      // Ragged last tile: rows past the end repeat the last row, so V stays
+      // finite where P is 0.
+      const int last = kv.len - 1 - t0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = min(trow[j], last);
+        const int32_t off = r * (int32_t)rs_bytes + (int32_t)((lpos ^ Lds::swz(trow[j])) << 4);
+        load_lds16(tb + off, dst + (16 * wave + 4 * j) * 256);
+      }
     }
   };
-  auto store_tile = [&](char *kl, char *vl) {
+
+  // V^T fragment addresses for the transposing reads (tile-relative): lane
+  // group G = lane/16 reads rows 16 ks + 8 half + 4 g + j, columns
+  // 32 db + 16 (G & 1) + 4 (lane & 3) .. +3.  The row part 16 ks + 8 half only
+  // adds a constant, so one base per (db, half) serves every ks.
+  const int tj = (lane & 15) >> 2, tc = lane & 3, tG = lane >> 4;
+  uint32_t vbase[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(kl + KTileLds<kKT>::offset(sr + 16 * i, sc)) = kr[i];
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x2 lo = {pack_lo16(vr[0][w], vr[1][w]), pack_lo16(vr[2][w], vr[3][w])};
-      u32x2 hi = {pack_hi16(vr[0][w], vr[1][w]), pack_hi16(vr[2][w], vr[3][w])};
-      *reinterpret_cast<u32x2 *>(vl + VtTileLds::offset(8 * sc + 2 * w, sr)) = lo;
-      *reinterpret_cast<u32x2 *>(vl + VtTileLds::offset(8 * sc + 2 * w + 1, sr)) = hi;
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * half + 4 * g + tj;
+      const int colv = 32 * db + 16 * (tG & 1) + 4 * tc;
+      vbase[db][half] = Lds::offset(row, colv >> 3) + ((colv & 7) << 1);
     }
+  // K fragment addresses: row kb*32 + col, chunk 2 st + g.
+  uint32_t kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = Lds::offset(col, 2 * st + g);
+
+  // S^T = K Q^T for one 64-key tile: 16 fragment reads feed 16 MFMAs on two
+  // independent accumulators.
+  auto qk = [&](const char *kl, f32x16 *sacc) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+    u32x4 kf[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kf[i] = lds_read_b128(kl, kbase[i >> 1] + (i & 1) * 32 * 256);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      sacc[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf[i]), qf[i >> 1], sacc[i & 1]);
   };
 
   const int ntiles = (kv.len + kKT - 1) / kKT;
-  load_tile(0);
-  for (int it = 0; it < ntiles; ++it) {
-    char *kl = smem + (it & 1) * kStageBytes;
-    char *vl = kl + kKBytes;
-    store_tile(kl, vl);
+  issue(kv.k, 0, kbuf(0));
+  issue(kv.v, 0, vbuf(0));
+  if (ntiles > 1) issue(kv.k, 1, kbuf(1));
+  wait_vmcnt0();
+  __syncthreads();
+  // One tile step: softmax of this tile's scores `sc` (computed one step
+  // earlier), next tile's scores into `sn`, then O += P V for this tile.
+  auto step = [&](int it, f32x16 *sc, f32x16 *sn) {
+    wait_vmcnt0();
     __syncthreads();
-    if (it + 1 < ntiles) load_tile((it + 1) * kKT);
+    if (it + 2 < ntiles) issue(kv.k, it + 2, kbuf(it));
+    if (it + 1 < ntiles) issue(kv.v, it + 1, vbuf(it + 1));
     const int valid = kv.len - it * kKT;
+    if (valid < kKT) {  // ragged last tile: keys past the end get no weight
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= valid) sc[kb][r] = -INFINITY;
+        }
+    }
+    float mx0 = sc[0][0], mx1 = sc[1][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      mx0 = fmaxf(mx0, sc[0][r]);
+      mx1 = fmaxf(mx1, sc[1][r]);
+    }
+    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
+    if (__any(mx > m + kLazyRescale)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    const float nm = -m;
 
-    // S^T for 64 keys x 32 queries: two 32x32 blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + col;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        u32x4 raw = lds_read_b128(kl, KTileLds<kKT>::offset(row, 2 * st + g));
-        s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), qf[st], s[kb]);
-      }
-    }
-    float mx = kNegBig;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float x = s[kb][r] * a.c;
-        x = key < valid ? x : -INFINITY;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[kb][r] - m);
-        ls += p;
-        s[kb][r] = p;
-      }
-    }
-    l += ls;
+    // Next tile's scores (independent of this tile's softmax).  On the last
+    // step this reads a stale buffer and the result is never used; it stays
+    // unconditional so that the MFMAs can interleave with the softmax.
+    qk(kbuf(it + 1), sn);
 
-    // P^T fragments: k-step ks covers keys 16 ks .. 16 ks + 15 of the tile.
+    // P^T fragments (k-step ks covers keys 16 ks .. 16 ks + 15) and the row
+    // sum of the bf16 weights the PV product uses.
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = ks >> 1, base = (ks & 1) * 8;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        bf16x2 p2 = pack_bf16(s[kb][base + e], s[kb][base + e + 1]);
+        const bf16x2 p2 = pack_bf16(fast_exp2(fmaf(sc[kb][base + e], c, nm)),
+                                    fast_exp2(fmaf(sc[kb][base + e + 1], c, nm)));
+        l = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l, false);
         pf[ks][e] = p2[0];
         pf[ks][e + 1] = p2[1];
       }
     }
-    // O^T += V^T P^T; lane (d = 32 db + col, g) feeds keys 16 ks + 4 g + 0..3
-    // and 16 ks + 8 + 4 g + 0..3, matching the key order of pf.
+    // O^T += V^T P^T; lane (d = 32 db + col, g) receives keys 16 ks + 4 g + 0..3
+    // and 16 ks + 8 + 4 g + 0..3, the key order of pf.
+    const char *vl = vbuf(it);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + col;
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x2 lo = lds_read_b64(vl, VtTileLds::offset(d, 4 * ks + g));
-        u32x2 hi = lds_read_b64(vl, VtTileLds::offset(d, 4 * ks + 2 + g));
-        u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 lo = lds_read_tr16(vl, vbase[db][0] + 16 * 256 * ks);
+        const u32x2 hi = lds_read_tr16(vl, vbase[db][1] + 16 * 256 * ks);
+        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
         o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[ks], o[db]);
       }
     }
-  }
+    // Interleave: K-fragment reads run four ahead of the 16 score MFMAs of
+    // the next tile, each followed by a slice of this tile's softmax; then the
+    // 16 PV MFMAs, two transposing reads ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
 
-  const float lt = l + swap_halves(l);
+  f32x16 sa[2], sb[2];
+  qk(kbuf(0), sa);
+  // Two steps per trip so the two score buffers swap roles without copies.
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, sa, sb);
+    step(it + 1, sb, sa);
+  }
+  if (it < ntiles) step(it, sa, sb);
+
+  const float lt = pair_sum(l);
   const float inv = 1.f / lt;
   if (qi < a.n_q) {
     __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;

@@ -44,37 +44,66 @@ __device__ __forceinline__ float swap_halves(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
+// v_permlane32_swap with both operands = v: one result holds v of the lower
+// half in both halves, the other v of the upper half.  Any symmetric
+// combination of the two is the lane-pair (l, l ^ 32) reduction.
+__device__ __forceinline__ float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their maxima):
+// waits until this wave's vector-memory loads, including loads that write
+// LDS directly, have completed.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16-byte global -> LDS copy without a register round trip
+// (global_load_lds_dwordx4).  The wave's 64 lanes fill the 1 KiB of LDS at
+// lds_wave_base (wave-uniform) in lane order, 16 bytes per lane.
+__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0,
+                                   0);
+}
+
 __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_convertvector(v, bf16x2);
 }
 
 // ---------------------------------------------------------------------------
-// K tile in LDS: KT rows (keys) x 128 bf16 (256 B); the 16-byte chunk c of row
-// j is stored at chunk position c ^ (j & 15), so that 16 consecutive rows read
-// at one chunk column hit 16 distinct bank groups.
+// K / V tiles in LDS: KT rows (keys) x 128 bf16 (256 B per row), row-major.
+// The 16-byte chunk c of row j sits at chunk position c ^ swz(j) with
+// swz(j) = ((j & 7) << 1) | ((j >> 3) & 1), which keeps three access
+// patterns free of bank conflicts:
+//   - 16 lanes writing the 16 chunks of one row;
+//   - 16 consecutive rows read at one chunk (the K fragments of S^T);
+//   - 4 consecutive rows x 2 adjacent chunks (the transposing V reads).
 template <int KT>
-struct KTileLds {
+struct KvTileLds {
   static constexpr int kBytes = KT * 256;
+  __device__ static __forceinline__ uint32_t swz(int row) {
+    return (uint32_t)(((row & 7) << 1) | ((row >> 3) & 1));
+  }
   __device__ static __forceinline__ uint32_t offset(int row, int chunk) {
-    return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4));
+    return (uint32_t)(row * 256) + (((uint32_t)chunk ^ swz(row)) << 4);
   }
 };
 
-// V^T tile in LDS: 128 rows (head dim) x KT keys bf16.  Keys are grouped in
-// 8-byte groups of 4; group G of row d sits at position G ^ swz(d) with
-// swz(d) = (d + (d >> 4)) & 15, spreading both the transposing writes (16
-// rows of one key group) and the fragment reads (32 rows of one key group)
-// over distinct banks.  KT must be 64 (16 groups per row).
-struct VtTileLds {
-  static constexpr int KT = 64;
-  static constexpr int kRowBytes = KT * 2;
-  static constexpr int kBytes = 128 * kRowBytes;
-  __device__ static __forceinline__ uint32_t offset(int d, int group) {
-    int swz = (d + (d >> 4)) & 15;
-    return (uint32_t)(d * kRowBytes + ((group ^ swz) << 3));
-  }
-};
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950).  Within each group of 16
+// lanes, lane s = 4 j + c supplies the address of 4 consecutive 16-bit
+// elements of row k0 + j at columns n0 + 4 c .. n0 + 4 c + 3; lane i of the
+// group receives column n0 + i of rows k0 .. k0 + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *base, uint32_t off) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  lds_s16x4 *p = (lds_s16x4 *)(base + off);  // generic -> LDS address space
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
 
 __device__ __forceinline__ u32x4 lds_read_b128(const char *base, uint32_t off) {
   return *reinterpret_cast<const u32x4 *>(base + off);

@@ -24,7 +24,7 @@ constexpr int kD = 128;
 constexpr int kKT = 64;
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
-constexpr int kKBytes = KTileLds<kKT>::kBytes;
+constexpr int kKBytes = KvTileLds<kKT>::kBytes;
 
 __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kKBytes];
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
     char *kl = smem + (it & 1) * kKBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(kl + KTileLds<kKT>::offset(sr + 16 * i, sc)) = kr[i];
+      *reinterpret_cast<u32x4 *>(kl + KvTileLds<kKT>::offset(sr + 16 * i, sc)) = kr[i];
     __syncthreads();
     if (it + 1 < ntiles) load_tile((it + 1) * kKT);
     const int valid = len - it * kKT;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
       const int row = kb2 * 32 + col;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        u32x4 raw = lds_read_b128(kl, KTileLds<kKT>::offset(row, 2 * st + g));
+        u32x4 raw = lds_read_b128(kl, KvTileLds<kKT>::offset(row, 2 * st + g));
         s[kb2] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), qf[st], s[kb2]);
       }
     }
