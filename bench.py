@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run the timed loop only (for rocprofv3), print nothing else")
+    ap.add_argument("--only", choices=["step", "compress", "attend", "dense", "copy"],
+                    default="step",
+                    help="with --profile-only: which call the loop runs ('copy': a plain "
+                         "1 GiB device-to-device tensor copy, the reference for counter "
+                         "calibration)")
     return ap.parse_args()
 
 
@@ -90,9 +95,18 @@ def measure(wname, args, fkv, torch, W):
         fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
         fkv.fkv_attend(L.desc, L.q, L.ckv, L.out)
 
-    ms_step = time_loop(step, layers, args.steps, args.warmup, torch)
     if args.profile_only:
+        fn = {"step": step,
+              "compress": lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
+                                                     w.budget_m, L.ckv),
+              "attend": lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv, L.out),
+              "dense": lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout)}[args.only]
+        if args.only == "attend":
+            for L in layers:
+                step(L)
+        time_loop(fn, layers, args.steps, args.warmup, torch)
         return None
+    ms_step = time_loop(step, layers, args.steps, args.warmup, torch)
     ms_compress = time_loop(lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
                                                        w.budget_m, L.ckv),
                             layers, args.steps, args.warmup, torch)
@@ -169,6 +183,13 @@ def main():
     from hybrid_kv_cache_amd import workloads as W
     fkv.load()
 
+    if args.profile_only and args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
     r = measure(args.workload, args, fkv, torch, W)
     if args.profile_only:
         return

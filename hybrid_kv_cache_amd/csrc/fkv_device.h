@@ -61,6 +61,38 @@ __device__ __forceinline__ float pair_sum(float v) {
 // LDS directly, have completed.
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for code that moves data into LDS only through
+// global_load_lds (whose completion the caller waits for explicitly with
+// s_waitcnt vmcnt): waits for this wave's own LDS reads and writes
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it carries no
+// memory fence, so copies still in flight for later tiles are not waited
+// for.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Buffer resource over `bytes` bytes starting at `base` (raw addressing,
+// stride 0).  Loads at offsets past the end return zeros; word 3 = 0x00020000
+// is the gfx9 data-format setting for untyped dword loads.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes
+// at rsrc + soffset + voffset land at lds_wave_base + 16 i.  lds_wave_base
+// must be wave-uniform and 1 KiB aligned.  Out-of-range lanes write zeros.
+__device__ __forceinline__ void buffer_load_lds16(buf_rsrc rsrc, uint32_t voffset,
+                                                  uint32_t soffset, void *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voffset, soffset, 0, 0);
+}
+
 // 16-byte global -> LDS copy without a register round trip
 // (global_load_lds_dwordx4).  The wave's 64 lanes fill the 1 KiB of LDS at
 // lds_wave_base (wave-uniform) in lane order, 16 bytes per lane.
@@ -78,16 +110,20 @@ __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
 // ---------------------------------------------------------------------------
 // K / V tiles in LDS: KT rows (keys) x 128 bf16 (256 B per row), row-major.
 // The 16-byte chunk c of row j sits at chunk position c ^ swz(j) with
-// swz(j) = ((j & 7) << 1) | ((j >> 3) & 1), which keeps three access
-// patterns free of bank conflicts:
+// swz(j) = ((j & 3) << 1) | ((j >> 2) & 1) | (j & 8).  For 32 banks (8 lanes
+// of 16 bytes per pass) as for 64 banks (16 lanes per pass) this keeps three
+// access patterns free of bank conflicts:
 //   - 16 lanes writing the 16 chunks of one row;
-//   - 16 consecutive rows read at one chunk (the K fragments of S^T);
-//   - 4 consecutive rows x 2 adjacent chunks (the transposing V reads).
+//   - 16 consecutive rows read at one chunk (the K fragments of S^T): every
+//     aligned group of 8 rows lands on 8 distinct positions modulo 8;
+//   - 4 consecutive rows x 2 adjacent chunks (the transposing V reads):
+//     bits 1-2 of swz differ between the 4 rows, so the 8 pieces land on 8
+//     distinct positions modulo 8.
 template <int KT>
 struct KvTileLds {
   static constexpr int kBytes = KT * 256;
   __device__ static __forceinline__ uint32_t swz(int row) {
-    return (uint32_t)(((row & 7) << 1) | ((row >> 3) & 1));
+    return (uint32_t)(((row & 3) << 1) | ((row >> 2) & 1) | (row & 8));
   }
   __device__ static __forceinline__ uint32_t offset(int row, int chunk) {
     return (uint32_t)(row * 256) + (((uint32_t)chunk ^ swz(row)) << 4);

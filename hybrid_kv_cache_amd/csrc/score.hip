@@ -12,7 +12,8 @@
 // (with all logits 0, every frame's value is exactly log2(T)).
 //
 // bf16 kernel: workgroup = 4 waves x 32 sampled queries, one frame of one
-// dynamic head; K rows of the frame stream through LDS in tiles of 64;
+// dynamic head; K rows of the frame are copied straight into a four-slot LDS
+// ring in tiles of 64 (three tiles in flight ahead of the one being read);
 // S^T = K Q^T on v_mfma_f32_32x32x16_bf16.
 #include "fkv_device.h"
 #include "fkv_launch.h"
@@ -24,10 +25,24 @@ constexpr int kD = 128;
 constexpr int kKT = 64;
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
-constexpr int kKBytes = KvTileLds<kKT>::kBytes;
+constexpr int kTileBytes = KvTileLds<kKT>::kBytes;
+constexpr int kAhead = 3;              // tiles in flight ahead of the one read (<= 3)
+constexpr int kRing = kAhead + 1;
+
+// Wait until at most `tiles` tile copies (4 loads each) of this wave remain
+// in flight: s_waitcnt vmcnt(8 / 4 / 0), gfx9 encoding.
+__device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
+  if (tiles >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (tiles == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kKBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kRing * kTileBytes];
+  typedef KvTileLds<kKT> Lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
@@ -36,6 +51,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   const int f = blockIdx.y;
   const int r = blockIdx.x * kBM + wave * 32 + col;   // sampled row
   const int64_t hd = (int64_t)a.H * kD;
+  const int64_t rs_bytes = hd * 2;
 
   bf16x8 qf[8];
   if (r < a.n_s) {
@@ -48,61 +64,88 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
     for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
   }
 
-  const __bf16 *kb = reinterpret_cast<const __bf16 *>(a.k) + (int64_t)f * a.T * hd + (int64_t)h * kD;
+  // K rows of frame f, head h: row j at kbase + j * H * D elements.
+  const char *kframe = reinterpret_cast<const char *>(a.k) +
+                       ((int64_t)f * a.T * hd + (int64_t)h * kD) * 2;
   const int len = a.T;
-  const int sc = tid & 15, sr = tid >> 4;
-  u32x4 kr[4];
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t0 + sr + 16 * i;
-      kr[i] = key < len ? ld16(kb + key * hd + sc * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-
-  float m = kNegBig, l = 0.f;
   const int ntiles = (len + kKT - 1) / kKT;
-  load_tile(0);
-  for (int it = 0; it < ntiles; ++it) {
-    char *kl = smem + (it & 1) * kKBytes;
+  const int lrow = lane >> 4, lpos = lane & 15;
+  auto ring = [&](int t) { return smem + (t % kRing) * kTileBytes; };
+  // Tile `it` -> LDS (4 direct copies per wave: rows 16 w + 4 j + lane/16).
+  // Copies through a buffer resource ending at the frame's last row: rows
+  // past the frame read as zeros (and are masked out of the sums).
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const buf_rsrc krsrc = make_rsrc(kframe, (uint32_t)((int64_t)(len - 1) * rs_bytes + kD * 2));
+  uint32_t goff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(kl + KvTileLds<kKT>::offset(sr + 16 * i, sc)) = kr[i];
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wave + 4 * j + lrow;
+    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4);
+  }
+  auto issue = [&](int it) -> bool {
+    if (it >= ntiles) return false;
+    const uint32_t soff = (uint32_t)((int64_t)it * kKT * rs_bytes);
+    char *dw = ring(it) + wave_s * (16 * 256);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(krsrc, goff[j], soff, dw + j * 1024);
+    return true;
+  };
+  uint32_t kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = Lds::offset(col, 2 * st + g);
+
+  for (int t = 0; t < kAhead; ++t) issue(t);
+  float m = kNegBig, l = 0.f;
+  for (int it = 0; it < ntiles; ++it) {
+    // Tile `it` must have landed; the (at most kAhead - 1) later ones may
+    // stay in flight.
+    wait_tiles_in_flight(min(kAhead - 1, ntiles - 1 - it));
     __syncthreads();
-    if (it + 1 < ntiles) load_tile((it + 1) * kKT);
+    issue(it + kAhead);
+    const char *kl = ring(it);
     const int valid = len - it * kKT;
 
     f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    u32x4 kf[16];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x16{};
-      const int row = kb2 * 32 + col;
+    for (int i = 0; i < 16; ++i) kf[i] = lds_read_b128(kl, kbase[i >> 1] + (i & 1) * 32 * 256);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        u32x4 raw = lds_read_b128(kl, KvTileLds<kKT>::offset(row, 2 * st + g));
-        s[kb2] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), qf[st], s[kb2]);
-      }
+    for (int i = 0; i < 16; ++i)
+      s[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf[i]), qf[i >> 1], s[i & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    float mx = kNegBig;
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+
+    if (valid < kKT) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int key = kb2 * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-        float x = s[kb2][q] * a.c;
-        x = key < valid ? x : -INFINITY;
-        s[kb2][q] = x;
-        mx = fmaxf(mx, x);
-      }
+        for (int q = 0; q < 16; ++q) {
+          const int key = kb * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+          if (key >= valid) s[kb][q] = -INFINITY;
+        }
     }
-    const float mnew = fmaxf(m, mx);
-    float ls = 0.f;
+    float mx0 = s[0][0], mx1 = s[1][0];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) ls += fast_exp2(s[kb2][q] - mnew);
+    for (int q = 1; q < 16; ++q) {
+      mx0 = fmaxf(mx0, s[0][q]);
+      mx1 = fmaxf(mx1, s[1][q]);
     }
-    l = l * fast_exp2(m - mnew) + ls;
+    const float mnew = fmaxf(m, fmaxf(mx0, mx1) * a.c);
+    const float nm = -mnew;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      ls0 += fast_exp2(fmaf(s[0][q], a.c, nm));
+      ls1 += fast_exp2(fmaf(s[1][q], a.c, nm));
+    }
+    l = l * fast_exp2(m - mnew) + (ls0 + ls1);
     m = mnew;
   }
   // Combine the two lanes that share a query column.

@@ -10,10 +10,10 @@
 // set is the min(m, F_h) best frames, ties broken by the lower frame index,
 // emitted in ascending frame order.
 //
-// One workgroup (4 waves) per head.  Dynamic heads: each wave walks a
-// quarter of the sampled queries, lane f holding frame f's log-sum-exp;
-// wave-wide max / sum give that query's per-frame masses, accumulated per
-// lane; the four partial sums are added in a fixed order (deterministic).
+// One workgroup (16 waves) per head.  Dynamic heads: each wave walks every
+// 16th sampled query, lane f holding frame f's log-sum-exp; wave-wide
+// max / sum give that query's per-frame masses, accumulated per lane; the
+// 16 partial sums are added in a fixed order (deterministic).
 // Wave 0 then sorts the (score, frame) pairs with a 64-lane bitonic network
 // and marks the first m_eff.  Every head finally writes its seg_idx entries
 // (bit rank = position), its offsets and its compaction slots.
@@ -39,8 +39,10 @@ __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib)
   return sa > sb || (sa == sb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  __shared__ float part[4][128];
+constexpr int kSelWaves = 16;
+
+__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
+  __shared__ float part[kSelWaves][128];
   __shared__ unsigned long long kept_bits_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
@@ -59,19 +61,30 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     if (tid == 0) kept_bits_s = a.static_bits[h];
     if (a.seg_score && tid < a.F_h) a.seg_score[(int64_t)h * a.F_h + tid] = __builtin_nanf("");
   } else {
-    // Per-lane accumulation of masses over this wave's sampled queries.
+    // Per-lane accumulation of masses over this wave's sampled queries, four
+    // rows per batch with their loads issued together.
     float acc0 = 0.f, acc1 = 0.f;
     const bool two = a.F_tot > 64;
-    for (int r = wave; r < a.n_s; r += 4) {
-      const float *row = a.lse + ((int64_t)di * a.n_s + r) * a.F_tot;
-      const float v0 = lane < a.F_tot ? row[lane] : -INFINITY;
-      const float v1 = (two && lane + 64 < a.F_tot) ? row[lane + 64] : -INFINITY;
-      const float M = wave_max(fmaxf(v0, v1));
-      const float e0 = fast_exp2(v0 - M), e1 = fast_exp2(v1 - M);
-      const float S = wave_sum(e0 + e1);
-      const float inv = 1.f / S;
-      acc0 += e0 * inv;
-      acc1 += e1 * inv;
+    const float *base = a.lse + (int64_t)di * a.n_s * a.F_tot;
+    for (int r0 = wave; r0 < a.n_s; r0 += 4 * kSelWaves) {
+      float v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u * kSelWaves;
+        const bool in = r < a.n_s;
+        const float *row = base + (int64_t)(in ? r : 0) * a.F_tot;
+        v0[u] = (in && lane < a.F_tot) ? row[lane] : -INFINITY;
+        v1[u] = (in && two && lane + 64 < a.F_tot) ? row[lane + 64] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (r0 + u * kSelWaves >= a.n_s) break;
+        const float M = wave_max(fmaxf(v0[u], v1[u]));
+        const float e0 = fast_exp2(v0[u] - M), e1 = fast_exp2(v1[u] - M);
+        const float inv = 1.f / wave_sum(e0 + e1);
+        acc0 += e0 * inv;
+        acc1 += e1 * inv;
+      }
     }
     part[wave][lane] = acc0;
     part[wave][lane + 64] = acc1;
@@ -79,7 +92,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     if (wave == 0) {
       float score = -INFINITY;
       if (lane < a.F_h) {
-        const float sum = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        float sum = part[0][lane];
+#pragma unroll
+        for (int w = 1; w < kSelWaves; ++w) sum += part[w][lane];
         score = sum / (float)a.n_s;
         if (a.seg_score) a.seg_score[(int64_t)h * a.F_h + lane] = score;
       }
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
 }  // namespace
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(select_kernel, dim3(a.H), dim3(64 * kSelWaves), 0, s, a);
   return hipGetLastError();
 }
 
