@@ -30,7 +30,7 @@ constexpr int kKT = 64;      // keys per tile
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
 constexpr int kTileBytes = KvTileLds<kKT>::kBytes;
-constexpr float kLazyRescale = 8.0f;         // log2 of the allowed growth
+constexpr float kLazyRescale = 8.0f;         // log2 of the allowed growth (other kernels)
 
 struct KvView {
   const __bf16 *k;
@@ -172,43 +172,73 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
           if (key >= valid) sc[kb][r] = -INFINITY;
         }
     }
-    float mx0 = sc[0][0], mx1 = sc[1][0];
+    // Exact maximum of this tile's scaled scores (lane pair combined).
+    auto tile_max = [&]() {
+      float mx0 = sc[0][0], mx1 = sc[1][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      mx0 = fmaxf(mx0, sc[0][r]);
-      mx1 = fmaxf(mx1, sc[1][r]);
-    }
-    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
-    if (__any(mx > m + kLazyRescale)) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
-      l *= alpha;
+      for (int r = 1; r < 16; ++r) {
+        mx0 = fmaxf(mx0, sc[0][r]);
+        mx1 = fmaxf(mx1, sc[1][r]);
+      }
+      return pair_max(fmaxf(mx0, mx1)) * c;
+    };
+    // Weights p = 2^(c s - m) of this tile as bf16 P^T fragments (k-step ks
+    // covers keys 16 ks .. 16 ks + 15), and their sum as the PV product
+    // sees them.
+    bf16x8 pf[4];
+    float lt = 0.f;
+    auto weights = [&]() {
+      const float nm = -m;
+      lt = 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    }
-    const float nm = -m;
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kb = ks >> 1, base = (ks & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 p2 = pack_bf16(fast_exp2(fmaf(sc[kb][base + e], c, nm)),
+                                      fast_exp2(fmaf(sc[kb][base + e + 1], c, nm)));
+          lt = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lt, false);
+          pf[ks][e] = p2[0];
+          pf[ks][e + 1] = p2[1];
+        }
+      }
+    };
+    // The reference m is the first tile's maximum and is raised only when a
+    // tile's weights sum past 2^64 (or overflow).  Any common reference gives
+    // the same O / l, so skipping the per-tile maximum changes nothing
+    // exactly, and weights up to 2^64 are far from fp32 / bf16 overflow.
+    if (it == 0) m = tile_max();
 
     // Next tile's scores (independent of this tile's softmax).  On the last
     // step this reads a stale buffer and the result is never used; it stays
     // unconditional so that the MFMAs can interleave with the softmax.
     qk(k_read, sn);
-
-    // P^T fragments (k-step ks covers keys 16 ks .. 16 ks + 15) and the row
-    // sum of the bf16 weights the PV product uses.
-    bf16x8 pf[4];
+    weights();
+    // K-fragment reads run four ahead of the 16 score MFMAs of the next
+    // tile, each followed by a slice of this tile's softmax.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb = ks >> 1, base = (ks & 1) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 p2 = pack_bf16(fast_exp2(fmaf(sc[kb][base + e], c, nm)),
-                                    fast_exp2(fmaf(sc[kb][base + e + 1], c, nm)));
-        l = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l, false);
-        pf[ks][e] = p2[0];
-        pf[ks][e + 1] = p2[1];
-      }
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    if (__any(!(lt <= 0x1p64f))) {
+      const float mnew = fmaxf(m, tile_max());
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      weights();
+    }
+    l += lt;
+
     // O^T += V^T P^T; lane (d = 32 db + col, g) receives keys 16 ks + 4 g + 0..3
     // and 16 ks + 8 + 4 g + 0..3, the key order of pf.
     const char *vl = v_read;
@@ -222,27 +252,12 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
         o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[ks], o[db]);
       }
     }
-    // Interleave: K-fragment reads run four ahead of the 16 score MFMAs of
-    // the next tile, each followed by a slice of this tile's softmax; then the
-    // 16 PV MFMAs, two transposing reads ahead.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
+    // PV: transposing reads two fragments ahead of the 16 MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 14; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };

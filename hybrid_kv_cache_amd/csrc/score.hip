@@ -131,22 +131,37 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
           if (key >= valid) s[kb][q] = -INFINITY;
         }
     }
-    float mx0 = s[0][0], mx1 = s[1][0];
+    // Per-lane running sum of 2^(c s - m).  The reference m is this lane's
+    // first-tile maximum and is raised only when a tile's sum passes 2^64 (or
+    // overflows): any reference gives the same log-sum-exp.
+    auto lane_max = [&]() {
+      float mx0 = s[0][0], mx1 = s[1][0];
 #pragma unroll
-    for (int q = 1; q < 16; ++q) {
-      mx0 = fmaxf(mx0, s[0][q]);
-      mx1 = fmaxf(mx1, s[1][q]);
-    }
-    const float mnew = fmaxf(m, fmaxf(mx0, mx1) * a.c);
-    const float nm = -mnew;
-    float ls0 = 0.f, ls1 = 0.f;
+      for (int q = 1; q < 16; ++q) {
+        mx0 = fmaxf(mx0, s[0][q]);
+        mx1 = fmaxf(mx1, s[1][q]);
+      }
+      return fmaxf(mx0, mx1) * a.c;
+    };
+    auto tile_sum = [&]() {
+      const float nm = -m;
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      ls0 += fast_exp2(fmaf(s[0][q], a.c, nm));
-      ls1 += fast_exp2(fmaf(s[1][q], a.c, nm));
+      for (int q = 0; q < 16; ++q) {
+        ls0 += fast_exp2(fmaf(s[0][q], a.c, nm));
+        ls1 += fast_exp2(fmaf(s[1][q], a.c, nm));
+      }
+      return ls0 + ls1;
+    };
+    if (it == 0) m = fmaxf(lane_max(), kNegBig);
+    float lt = tile_sum();
+    if (__any(!(lt <= 0x1p64f))) {
+      const float mnew = fmaxf(m, lane_max());
+      l *= fast_exp2(m - mnew);
+      m = mnew;
+      lt = tile_sum();
     }
-    l = l * fast_exp2(m - mnew) + (ls0 + ls1);
-    m = mnew;
+    l += lt;
   }
   // Combine the two lanes that share a query column.
   const float m2 = swap_halves(m), l2 = swap_halves(l);

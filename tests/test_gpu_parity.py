@@ -137,3 +137,26 @@ def test_deterministic_across_runs():
         outs.append((res["seg_score"].copy(), fkv.to_host(ckv.k).copy(), fkv.to_host(out)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b, equal_nan=True) if a.dtype.kind == "f" else np.array_equal(a, b)
+
+
+def test_late_frames_with_much_larger_scores():
+    """Keys of the current chunk scaled up so that their logits exceed the
+    first tiles' by far more than 2^64 in weight: the running reference must
+    be raised mid-stream (score and attention kernels) with exact results."""
+    for dtype, D in (("bf16", 128), ("f32", 64)):
+        w = W.small_workload(name=f"late_{dtype}", dtype=dtype, head_dim=D,
+                             tokens_per_frame=80, num_heads=3, hist_frames=6, budget_m=3,
+                             num_static=1, seed=21)
+        inp = W.generate_layer(w)
+        q = inp.as_f32("q")
+        k = inp.as_f32("k").copy()
+        cur = slice(w.hist_frames * w.tokens_per_frame, None)
+        # align the current chunk's keys with each head's mean query, x40
+        for h in range(w.num_heads):
+            u = q[:, h].mean(axis=0)
+            k[cur, h] = 40.0 * u / max(np.linalg.norm(u), 1e-6) * np.sqrt(D) + 0.1 * k[cur, h]
+        if dtype == "bf16":
+            inp.k = W.round_to_bf16_bits(k)
+        else:
+            inp.k = k.astype(np.float32)
+        full_case(w, inp)
