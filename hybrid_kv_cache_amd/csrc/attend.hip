@@ -70,8 +70,20 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y;
-  const int qi = blockIdx.x * kBM + wave * 32 + col;
+  // XCD-aware tile order: workgroups are handed to the 8 XCDs round-robin,
+  // so workgroup b runs on XCD b % 8.  Give each XCD a contiguous range of
+  // (head, query tile) pairs so that the workgroups sharing an L2 stream the
+  // same head's K/V at the same time.
+  const int ntq = (a.n_q + kBM - 1) / kBM;
+  int h, qt;
+  {
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int x = b & 7, slot = b >> 3;
+    const int pair = x * (nb >> 3) + min(x, nb & 7) + slot;
+    h = pair / ntq;
+    qt = pair - h * ntq;
+  }
+  const int qi = qt * kBM + wave * 32 + col;
   const KvView kv = kv_view(a, h);
   const int64_t rs_bytes = kv.rs * 2;
 
@@ -599,7 +611,7 @@ hipError_t launch_attend_bf16(const AttendArgs &a, hipStream_t s) {
     dim3 grid((a.n_q + kWBM - 1) / kWBM, a.H);
     hipLaunchKernelGGL(attend_bf16_w64_kernel, grid, dim3(256), kWLdsBytes, s, a);
   } else {
-    dim3 grid((a.n_q + kBM - 1) / kBM, a.H);
+    dim3 grid(((a.n_q + kBM - 1) / kBM) * a.H);
     hipLaunchKernelGGL(attend_bf16_kernel, grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
