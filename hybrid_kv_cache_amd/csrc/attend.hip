@@ -308,94 +308,71 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   }
 }
 
-// Wide-wave variant: one workgroup = 4 waves x 64 queries of one head, one
-// wave per SIMD.  Every K and V fragment read from LDS feeds two MFMAs (two
-// 32-query groups), halving LDS instructions per MFMA.  Key tiles of 32;
-// K and V tiles live in rings of kRing slots, the copies for K(t+kAhead+1)
-// and V(t+kAhead) being issued at step t, kAhead steps before they are read.
-constexpr int kWWaves = 4;
-constexpr int kWBM = 64 * kWWaves;
-constexpr int kWKT = 32;
-constexpr int kWTileBytes = KvTileLds<kWKT>::kBytes;
-constexpr int kAhead = 3;
-constexpr int kRing = kAhead + 1;
-constexpr int kWLdsBytes = 2 * kRing * kWTileBytes;
+// Large-tile variant: one workgroup = 8 waves x 32 queries of one head (two
+// waves per SIMD, one workgroup per CU), key tiles of 128 staged through
+// 128 KiB of LDS (K and V double-buffered).  Half as many barriers and
+// per-tile fixed costs per MFMA as the 64-key kernel; no score double
+// buffer (the second wave on each SIMD covers the MFMA -> softmax latency).
+constexpr int kLWaves = 8;
+constexpr int kLBM = 32 * kLWaves;
+constexpr int kLKT = 128;
+constexpr int kLTileBytes = KvTileLds<kLKT>::kBytes;
 
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  // s_waitcnt vmcnt(n) for the counts used below (gfx9 encoding).
-  if (n >= 4)
-    __builtin_amdgcn_s_waitcnt(0x0F74);
-  else if (n >= 2)
-    __builtin_amdgcn_s_waitcnt(0x0F72);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-__global__ __launch_bounds__(256, 1) void attend_bf16_w64_kernel(AttendArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  typedef KvTileLds<kWKT> Lds;
+__global__ __launch_bounds__(512, 1) void attend_bf16_k128_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(1024))) char sk0[kLTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sk1[kLTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sv0[kLTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sv1[kLTileBytes];
+  typedef KvTileLds<kLKT> Lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y;
-  const int q0 = blockIdx.x * kWBM + wave * 64 + col;   // query of group 0; group 1 is +32
+  const int ntq = (a.n_q + kLBM - 1) / kLBM;
+  int h, qt;
+  {
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int x = b & 7, slot = b >> 3;
+    const int pair = x * (nb >> 3) + min(x, nb & 7) + slot;
+    h = pair / ntq;
+    qt = pair - h * ntq;
+  }
+  const int qi = qt * kLBM + wave * 32 + col;
   const KvView kv = kv_view(a, h);
   const int64_t rs_bytes = kv.rs * 2;
-  auto kring = [&](int t) { return smem + (t % kRing) * kWTileBytes; };
-  auto vring = [&](int t) { return smem + (kRing + t % kRing) * kWTileBytes; };
 
-  bf16x8 qf[2][8];
+  bf16x8 qf[8];
+  if (qi < a.n_q) {
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)qi * a.H + h) * kD + 8 * g;
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
-    const int qi = q0 + 32 * qg;
-    if (qi < a.n_q) {
-      const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)qi * a.H + h) * kD + 8 * g;
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
+  } else {
 #pragma unroll
-      for (int st = 0; st < 8; ++st) qf[qg][st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
-    } else {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) qf[qg][st] = bf16x8{};
-    }
+    for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
   }
-
-  f32x16 o[2][4];
+  f32x16 o[4];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[qg][db] = f32x16{};
-  float m0 = kNegBig, m1 = kNegBig, l0 = 0.f, l1 = 0.f;
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m = kNegBig, l = 0.f;
   const float c = a.c;
 
-  // Staging: wave w fills rows 8 w .. 8 w + 7 of a tile (two instructions of
-  // four rows); lane i lands at row 8 w + 4 j + i/16, chunk position i%16.
+  // Staging: wave w fills tile rows 16 w .. 16 w + 15 (4 instructions).
   const int lrow = lane >> 4, lpos = lane & 15;
-  int32_t goff[2];
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t range_bytes = (uint32_t)((int64_t)(kv.len - 1) * rs_bytes + kD * 2);
+  const buf_rsrc krsrc = make_rsrc(kv.k, range_bytes);
+  const buf_rsrc vrsrc = make_rsrc(kv.v, range_bytes);
+  uint32_t goff[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * wave + 4 * j + lrow;
-    goff[j] = row * (int32_t)rs_bytes + (int32_t)((lpos ^ Lds::swz(row)) << 4);
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wave + 4 * j + lrow;
+    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4);
   }
-  const int ntiles = (kv.len + kWKT - 1) / kWKT;
-  auto issue = [&](const __bf16 *src, int it, char *dst) -> int {
-    if (it >= ntiles) return 0;
-    const int t0 = it * kWKT;
-    const char *tb = reinterpret_cast<const char *>(src) + (int64_t)t0 * rs_bytes;
-    if (t0 + kWKT <= kv.len) {
+  auto issue = [&](const buf_rsrc &rsrc, int it, char *dst) {
+    const uint32_t soff = (uint32_t)((int64_t)it * kLKT * rs_bytes);
+    char *dw = dst + wave_s * (16 * 256);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_lds16(tb + goff[j], dst + (8 * wave + 4 * j) * 256);
-    } else {
-      const int last = kv.len - 1 - t0;   // rows past the end repeat the last row
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 8 * wave + 4 * j + lrow;
-        const int r = min(row, last);
-        const int32_t off = r * (int32_t)rs_bytes + (int32_t)((lpos ^ Lds::swz(row)) << 4);
-        load_lds16(tb + off, dst + (8 * wave + 4 * j) * 256);
-      }
-    }
-    return 2;
+    for (int j = 0; j < 4; ++j) buffer_load_lds16(rsrc, goff[j], soff, dw + j * 1024);
   };
-
   const int tj = (lane & 15) >> 2, tc = lane & 3, tG = lane >> 4;
   uint32_t vbase[4][2];
 #pragma unroll
@@ -410,122 +387,127 @@ __global__ __launch_bounds__(256, 1) void attend_bf16_w64_kernel(AttendArgs a) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) kbase[st] = Lds::offset(col, 2 * st + g);
 
-  // S^T for 32 keys x 64 queries: sacc[qg].
-  auto qk = [&](const char *kl, f32x16 &s0, f32x16 &s1) {
-    s0 = f32x16{};
-    s1 = f32x16{};
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const u32x4 kf = lds_read_b128(kl, kbase[st]);
-      s0 = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[0][st], s0);
-      s1 = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[1][st], s1);
+  const int ntiles = (kv.len + kLKT - 1) / kLKT;
+  auto step = [&](auto par, int it) {
+    constexpr int P = decltype(par)::value;
+    char *const k_read = P ? sk1 : sk0;
+    char *const k_fill = P ? sk0 : sk1;
+    char *const v_read = P ? sv1 : sv0;
+    char *const v_fill = P ? sv0 : sv1;
+    wait_vmcnt0();
+    lds_barrier();
+    if (it + 1 < ntiles) {
+      issue(krsrc, it + 1, k_fill);
+      issue(vrsrc, it + 1, v_fill);
     }
-  };
-
-  auto step = [&](int it, f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int prev_issued) {
-    // Tiles it+1 (K) and it (V) were issued kAhead - 1 steps ago or earlier;
-    // only the copies of the previous step may still be in flight.
-    wait_vmcnt_le(prev_issued);
-    __syncthreads();
-    int issued = issue(kv.k, it + kAhead + 1, kring(it + kAhead + 1));
-    issued += issue(kv.v, it + kAhead, vring(it + kAhead));
-    const int valid = kv.len - it * kWKT;
-    if (valid < kWKT) {
+    // S^T for 128 keys x 32 queries: four 32x32 blocks.
+    f32x16 sc[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= valid) {
-          c0[r] = -INFINITY;
-          c1[r] = -INFINITY;
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int st = i >> 2, kb = i & 3;
+      const u32x4 kf = lds_read_b128(k_read, kbase[st] + kb * 32 * 256);
+      sc[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[st], sc[kb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 26; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+
+    const int valid = kv.len - it * kLKT;
+    if (valid < kLKT) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= valid) sc[kb][r] = -INFINITY;
+        }
+    }
+    auto tile_max = [&]() {
+      float mx0 = sc[0][0], mx1 = sc[1][0], mx2 = sc[2][0], mx3 = sc[3][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        mx0 = fmaxf(mx0, sc[0][r]);
+        mx1 = fmaxf(mx1, sc[1][r]);
+        mx2 = fmaxf(mx2, sc[2][r]);
+        mx3 = fmaxf(mx3, sc[3][r]);
+      }
+      return pair_max(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3))) * c;
+    };
+    bf16x8 pf[8];
+    float lt = 0.f;
+    auto weights = [&]() {
+      const float nm = -m;
+      lt = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int kb = ks >> 1, base = (ks & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 p2 = pack_bf16(fast_exp2(fmaf(sc[kb][base + e], c, nm)),
+                                      fast_exp2(fmaf(sc[kb][base + e + 1], c, nm)));
+          lt = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lt, false);
+          pf[ks][e] = p2[0];
+          pf[ks][e + 1] = p2[1];
         }
       }
-    }
-    float a0 = c0[0], a1 = c1[0];
+    };
+    if (it == 0) m = tile_max();
+    weights();
+    if (__any(!(lt <= 0x1p64f))) {
+      const float mnew = fmaxf(m, tile_max());
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      a0 = fmaxf(a0, c0[r]);
-      a1 = fmaxf(a1, c1[r]);
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      weights();
     }
-    const float mx0 = pair_max(a0) * c, mx1 = pair_max(a1) * c;
-    if (__any(mx0 > m0 + kLazyRescale || mx1 > m1 + kLazyRescale)) {
-      const float mn0 = fmaxf(m0, mx0), mn1 = fmaxf(m1, mx1);
-      const float al0 = fast_exp2(m0 - mn0), al1 = fast_exp2(m1 - mn1);
-      m0 = mn0;
-      m1 = mn1;
-      l0 *= al0;
-      l1 *= al1;
+    l += lt;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        o[0][db] *= al0;
-        o[1][db] *= al1;
-      }
-    }
-    // Next tile's scores (unconditional: on the last step the buffer is stale
-    // and the result unused).
-    qk(kring(it + 1), n0, n1);
-    bf16x8 pf[2][2];
-    const float nm0 = -m0, nm1 = -m1;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int r = ks * 8 + e;
-        const bf16x2 p0 = pack_bf16(fast_exp2(fmaf(c0[r], c, nm0)), fast_exp2(fmaf(c0[r + 1], c, nm0)));
-        const bf16x2 p1 = pack_bf16(fast_exp2(fmaf(c1[r], c, nm1)), fast_exp2(fmaf(c1[r + 1], c, nm1)));
-        l0 = __builtin_amdgcn_fdot2_f32_bf16(p0, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l0, false);
-        l1 = __builtin_amdgcn_fdot2_f32_bf16(p1, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l1, false);
-        pf[0][ks][e] = p0[0];
-        pf[0][ks][e + 1] = p0[1];
-        pf[1][ks][e] = p1[0];
-        pf[1][ks][e + 1] = p1[1];
-      }
-    }
-    const char *vl = vring(it);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = lds_read_tr16(vl, vbase[db][0] + 16 * 256 * ks);
-        const u32x2 hi = lds_read_tr16(vl, vbase[db][1] + 16 * 256 * ks);
+        const u32x2 lo = lds_read_tr16(v_read, vbase[db][0] + 16 * 256 * ks);
+        const u32x2 hi = lds_read_tr16(v_read, vbase[db][1] + 16 * 256 * ks);
         const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        o[0][db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[0][ks], o[0][db]);
-        o[1][db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[1][ks], o[1][db]);
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[ks], o[db]);
       }
     }
-    return issued;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 30; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
-  // Prologue: tiles 0..kAhead of K and 0..kAhead-1 of V.
-  for (int t = 0; t <= kAhead; ++t) issue(kv.k, t, kring(t));
-  for (int t = 0; t < kAhead; ++t) issue(kv.v, t, vring(t));
-  wait_vmcnt0();
-  __syncthreads();
-  f32x16 sa0, sa1, sb0, sb1;
-  qk(kring(0), sa0, sa1);
-  int prev = 0;
+  issue(krsrc, 0, sk0);
+  issue(vrsrc, 0, sv0);
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    prev = step(it, sa0, sa1, sb0, sb1, prev);
-    prev = step(it + 1, sb0, sb1, sa0, sa1, prev);
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
-  if (it < ntiles) step(it, sa0, sa1, sb0, sb1, prev);
+  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
 
+  const float inv = 1.f / pair_sum(l);
+  if (qi < a.n_q) {
+    __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
-    const int qi = q0 + 32 * qg;
-    const float inv = 1.f / pair_sum(qg ? l1 : l0);
-    if (qi < a.n_q) {
-      __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int d0 = db * 32 + 8 * rr + 4 * g;
-          bf16x2 lo = pack_bf16(o[qg][db][4 * rr] * inv, o[qg][db][4 * rr + 1] * inv);
-          bf16x2 hi = pack_bf16(o[qg][db][4 * rr + 2] * inv, o[qg][db][4 * rr + 3] * inv);
-          u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          *reinterpret_cast<u32x2 *>(op + d0) = w;
-        }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = db * 32 + 8 * rr + 4 * g;
+        bf16x2 lo = pack_bf16(o[db][4 * rr] * inv, o[db][4 * rr + 1] * inv);
+        bf16x2 hi = pack_bf16(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
+        u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        *reinterpret_cast<u32x2 *>(op + d0) = w;
       }
     }
   }
@@ -599,17 +581,10 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
 
 hipError_t launch_attend_bf16(const AttendArgs &a, hipStream_t s) {
   if (a.D != kD) return hipErrorInvalidValue;
-  static const bool wide = getenv("FKV_ATTEND_W64") && getenv("FKV_ATTEND_W64")[0] == '1';
-  if (wide) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)attend_bf16_w64_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kWLdsBytes);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    dim3 grid((a.n_q + kWBM - 1) / kWBM, a.H);
-    hipLaunchKernelGGL(attend_bf16_w64_kernel, grid, dim3(256), kWLdsBytes, s, a);
+  static const bool large = getenv("FKV_ATTEND_K128") && getenv("FKV_ATTEND_K128")[0] == '1';
+  if (large) {
+    dim3 grid(((a.n_q + kLBM - 1) / kLBM) * a.H);
+    hipLaunchKernelGGL(attend_bf16_k128_kernel, grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(((a.n_q + kBM - 1) / kBM) * a.H);
     hipLaunchKernelGGL(attend_bf16_kernel, grid, dim3(256), 0, s, a);

@@ -78,9 +78,19 @@ __device__ __forceinline__ void lds_barrier() {
 // Buffer resource over `bytes` bytes starting at `base` (raw addressing,
 // stride 0).  Loads at offsets past the end return zeros; word 3 = 0x00020000
 // is the gfx9 data-format setting for untyped dword loads.
+// The base and size must be wave-uniform; they are passed through
+// readfirstlane so that the compiler keeps the descriptor in scalar registers
+// (a descriptor it believes divergent costs a loop over lanes per load).
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+  // readfirstlane returns int: go through uint32_t so neither half is
+  // sign-extended when the 64-bit address is put back together.
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t up = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const int ub = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(up), (short)0, ub,
                                            0x00020000);
 }
 

@@ -47,7 +47,10 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int di = blockIdx.z;
-  const int h = a.dyn_heads[di];
+  // The head index is read from a kernel-argument array with a runtime
+  // index; readfirstlane tells the compiler it is wave-uniform, so the K
+  // buffer resource stays in scalar registers.
+  const int h = __builtin_amdgcn_readfirstlane(a.dyn_heads[di]);
   const int f = blockIdx.y;
   const int r = blockIdx.x * kBM + wave * 32 + col;   // sampled row
   const int64_t hd = (int64_t)a.H * kD;
