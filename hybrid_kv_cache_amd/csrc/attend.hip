@@ -7,19 +7,21 @@
 //
 // bf16 kernel (D = 128): one workgroup = 4 waves x 32 queries of one head.
 // K and V tiles of 64 keys are copied row-major from global memory straight
-// into LDS (global_load_lds, double buffered, one barrier per tile, the next
-// tile's copies in flight during the current tile's math).  Scores S^T = K Q^T and the output
-// O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
-// V^T operand comes straight from the row-major tile through transposing LDS
-// reads.  Softmax: online form in base 2 with the logit scale folded into
-// one FMA per score; the running maximum is raised (and the accumulator
-// rescaled) only when a tile's maximum exceeds it by more than 2^8, which
-// leaves the result exact (the final division uses the same reference) and
-// removes the per-tile rescale of the 64 accumulator registers.
+// into LDS (buffer loads with the LDS destination, double buffered, one
+// barrier per tile, the next tiles' copies in flight during the current
+// tile's math).  Scores S^T = K Q^T and the output O^T = V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the V^T operand comes
+// straight from the row-major tile through transposing LDS reads.  Softmax
+// in base 2 with the logit scale folded into one FMA per score.  The
+// reference subtracted before exponentiation is the first tile's maximum and
+// is raised (with a rescale of the accumulators) only when a tile's weight
+// sum would pass 2^64: any reference gives the same normalised result, so
+// the per-tile maximum and rescale are gone from the common path.
+// Workgroups are spread so that each XCD (blockIdx % 8) runs a contiguous
+// range of (head, query tile) pairs and shares that head's K/V in its L2.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace fkv {
@@ -308,211 +310,6 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   }
 }
 
-// Large-tile variant: one workgroup = 8 waves x 32 queries of one head (two
-// waves per SIMD, one workgroup per CU), key tiles of 128 staged through
-// 128 KiB of LDS (K and V double-buffered).  Half as many barriers and
-// per-tile fixed costs per MFMA as the 64-key kernel; no score double
-// buffer (the second wave on each SIMD covers the MFMA -> softmax latency).
-constexpr int kLWaves = 8;
-constexpr int kLBM = 32 * kLWaves;
-constexpr int kLKT = 128;
-constexpr int kLTileBytes = KvTileLds<kLKT>::kBytes;
-
-__global__ __launch_bounds__(512, 1) void attend_bf16_k128_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(1024))) char sk0[kLTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sk1[kLTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sv0[kLTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sv1[kLTileBytes];
-  typedef KvTileLds<kLKT> Lds;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, g = lane >> 5;
-  const int ntq = (a.n_q + kLBM - 1) / kLBM;
-  int h, qt;
-  {
-    const int nb = gridDim.x, b = blockIdx.x;
-    const int x = b & 7, slot = b >> 3;
-    const int pair = x * (nb >> 3) + min(x, nb & 7) + slot;
-    h = pair / ntq;
-    qt = pair - h * ntq;
-  }
-  const int qi = qt * kLBM + wave * 32 + col;
-  const KvView kv = kv_view(a, h);
-  const int64_t rs_bytes = kv.rs * 2;
-
-  bf16x8 qf[8];
-  if (qi < a.n_q) {
-    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)qi * a.H + h) * kD + 8 * g;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
-  } else {
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
-  }
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m = kNegBig, l = 0.f;
-  const float c = a.c;
-
-  // Staging: wave w fills tile rows 16 w .. 16 w + 15 (4 instructions).
-  const int lrow = lane >> 4, lpos = lane & 15;
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t range_bytes = (uint32_t)((int64_t)(kv.len - 1) * rs_bytes + kD * 2);
-  const buf_rsrc krsrc = make_rsrc(kv.k, range_bytes);
-  const buf_rsrc vrsrc = make_rsrc(kv.v, range_bytes);
-  uint32_t goff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * wave + 4 * j + lrow;
-    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4);
-  }
-  auto issue = [&](const buf_rsrc &rsrc, int it, char *dst) {
-    const uint32_t soff = (uint32_t)((int64_t)it * kLKT * rs_bytes);
-    char *dw = dst + wave_s * (16 * 256);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) buffer_load_lds16(rsrc, goff[j], soff, dw + j * 1024);
-  };
-  const int tj = (lane & 15) >> 2, tc = lane & 3, tG = lane >> 4;
-  uint32_t vbase[4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int row = 8 * half + 4 * g + tj;
-      const int colv = 32 * db + 16 * (tG & 1) + 4 * tc;
-      vbase[db][half] = Lds::offset(row, colv >> 3) + ((colv & 7) << 1);
-    }
-  uint32_t kbase[8];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) kbase[st] = Lds::offset(col, 2 * st + g);
-
-  const int ntiles = (kv.len + kLKT - 1) / kLKT;
-  auto step = [&](auto par, int it) {
-    constexpr int P = decltype(par)::value;
-    char *const k_read = P ? sk1 : sk0;
-    char *const k_fill = P ? sk0 : sk1;
-    char *const v_read = P ? sv1 : sv0;
-    char *const v_fill = P ? sv0 : sv1;
-    wait_vmcnt0();
-    lds_barrier();
-    if (it + 1 < ntiles) {
-      issue(krsrc, it + 1, k_fill);
-      issue(vrsrc, it + 1, v_fill);
-    }
-    // S^T for 128 keys x 32 queries: four 32x32 blocks.
-    f32x16 sc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int st = i >> 2, kb = i & 3;
-      const u32x4 kf = lds_read_b128(k_read, kbase[st] + kb * 32 * 256);
-      sc[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[st], sc[kb]);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 26; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-
-    const int valid = kv.len - it * kLKT;
-    if (valid < kLKT) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= valid) sc[kb][r] = -INFINITY;
-        }
-    }
-    auto tile_max = [&]() {
-      float mx0 = sc[0][0], mx1 = sc[1][0], mx2 = sc[2][0], mx3 = sc[3][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        mx0 = fmaxf(mx0, sc[0][r]);
-        mx1 = fmaxf(mx1, sc[1][r]);
-        mx2 = fmaxf(mx2, sc[2][r]);
-        mx3 = fmaxf(mx3, sc[3][r]);
-      }
-      return pair_max(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3))) * c;
-    };
-    bf16x8 pf[8];
-    float lt = 0.f;
-    auto weights = [&]() {
-      const float nm = -m;
-      lt = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int kb = ks >> 1, base = (ks & 1) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 p2 = pack_bf16(fast_exp2(fmaf(sc[kb][base + e], c, nm)),
-                                      fast_exp2(fmaf(sc[kb][base + e + 1], c, nm)));
-          lt = __builtin_amdgcn_fdot2_f32_bf16(p2, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lt, false);
-          pf[ks][e] = p2[0];
-          pf[ks][e + 1] = p2[1];
-        }
-      }
-    };
-    if (it == 0) m = tile_max();
-    weights();
-    if (__any(!(lt <= 0x1p64f))) {
-      const float mnew = fmaxf(m, tile_max());
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      weights();
-    }
-    l += lt;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = lds_read_tr16(v_read, vbase[db][0] + 16 * 256 * ks);
-        const u32x2 hi = lds_read_tr16(v_read, vbase[db][1] + 16 * 256 * ks);
-        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, raw), pf[ks], o[db]);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 30; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-  };
-
-  issue(krsrc, 0, sk0);
-  issue(vrsrc, 0, sv0);
-  int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
-
-  const float inv = 1.f / pair_sum(l);
-  if (qi < a.n_q) {
-    __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = db * 32 + 8 * rr + 4 * g;
-        bf16x2 lo = pack_bf16(o[db][4 * rr] * inv, o[db][4 * rr + 1] * inv);
-        bf16x2 hi = pack_bf16(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
-        u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<u32x2 *>(op + d0) = w;
-      }
-    }
-  }
-}
-
 // fp32 path (small shapes): one thread per query, keys staged 32 at a time in
 // LDS and read by broadcast; exact online softmax per key.
 template <int D>
@@ -581,14 +378,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
 
 hipError_t launch_attend_bf16(const AttendArgs &a, hipStream_t s) {
   if (a.D != kD) return hipErrorInvalidValue;
-  static const bool large = getenv("FKV_ATTEND_K128") && getenv("FKV_ATTEND_K128")[0] == '1';
-  if (large) {
-    dim3 grid(((a.n_q + kLBM - 1) / kLBM) * a.H);
-    hipLaunchKernelGGL(attend_bf16_k128_kernel, grid, dim3(512), 0, s, a);
-  } else {
-    dim3 grid(((a.n_q + kBM - 1) / kBM) * a.H);
-    hipLaunchKernelGGL(attend_bf16_kernel, grid, dim3(256), 0, s, a);
-  }
+  dim3 grid(((a.n_q + kBM - 1) / kBM) * a.H);
+  hipLaunchKernelGGL(attend_bf16_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,10 +10,10 @@
 // set is the min(m, F_h) best frames, ties broken by the lower frame index,
 // emitted in ascending frame order.
 //
-// One workgroup (16 waves) per head.  Dynamic heads: each wave walks every
-// 16th sampled query, lane f holding frame f's log-sum-exp; wave-wide
-// max / sum give that query's per-frame masses, accumulated per lane; the
-// 16 partial sums are added in a fixed order (deterministic).
+// One workgroup (4 waves) per head.  Dynamic heads: one sampled query per
+// thread at a time, the softmax over its frames in registers, masses summed
+// per thread, then over each wave and over the 4 waves in a fixed order
+// (deterministic).
 // Wave 0 then sorts the (score, frame) pairs with a 64-lane bitonic network
 // and marks the first m_eff.  Every head finally writes its seg_idx entries
 // (bit rank = position), its offsets and its compaction slots.
@@ -39,10 +39,48 @@ __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib)
   return sa > sb || (sa == sb && ia < ib);
 }
 
-constexpr int kSelWaves = 16;
+constexpr int kSelWaves = 4;
+
+// Masses of one dynamic head: thread t takes sampled queries t, t + 256, ...;
+// for each, the F_tot frame log-sum-exps (base 2) become a softmax over
+// frames, whose first F_h entries are added to per-thread sums.  The sums
+// are reduced over each wave with shuffles and stored per wave in part[w][f].
+template <int FT>
+__device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int F_h,
+                                                  float (*part)[64], int tid, int lane,
+                                                  int wave) {
+  float acc[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) acc[f] = 0.f;
+  for (int r = tid; r < n_s; r += 64 * kSelWaves) {
+    const float *row = base + (int64_t)r * F_tot;
+    float v[FT];
+#pragma unroll
+    for (int f = 0; f < FT; ++f) v[f] = f < F_tot ? row[f] : -INFINITY;
+    float M = v[0];
+#pragma unroll
+    for (int f = 1; f < FT; ++f) M = fmaxf(M, v[f]);
+    float S = 0.f;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      v[f] = fast_exp2(v[f] - M);
+      S += v[f];
+    }
+    const float inv = 1.f / S;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) acc[f] += v[f] * inv;
+  }
+#pragma unroll
+  for (int f = 0; f < FT && f < 64; ++f) {
+    if (f < F_h) {
+      const float x = wave_sum(acc[f]);
+      if (lane == 0) part[wave][f] = x;
+    }
+  }
+}
 
 __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
-  __shared__ float part[kSelWaves][128];
+  __shared__ float part[kSelWaves][64];
   __shared__ unsigned long long kept_bits_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
@@ -61,33 +99,14 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
     if (tid == 0) kept_bits_s = a.static_bits[h];
     if (a.seg_score && tid < a.F_h) a.seg_score[(int64_t)h * a.F_h + tid] = __builtin_nanf("");
   } else {
-    // Per-lane accumulation of masses over this wave's sampled queries, four
-    // rows per batch with their loads issued together.
-    float acc0 = 0.f, acc1 = 0.f;
-    const bool two = a.F_tot > 64;
+    // One sampled query per thread: its frame values in registers, softmax
+    // over frames, masses accumulated per thread; then a fixed-order
+    // reduction over threads (deterministic).
     const float *base = a.lse + (int64_t)di * a.n_s * a.F_tot;
-    for (int r0 = wave; r0 < a.n_s; r0 += 4 * kSelWaves) {
-      float v0[4], v1[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * kSelWaves;
-        const bool in = r < a.n_s;
-        const float *row = base + (int64_t)(in ? r : 0) * a.F_tot;
-        v0[u] = (in && lane < a.F_tot) ? row[lane] : -INFINITY;
-        v1[u] = (in && two && lane + 64 < a.F_tot) ? row[lane + 64] : -INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (r0 + u * kSelWaves >= a.n_s) break;
-        const float M = wave_max(fmaxf(v0[u], v1[u]));
-        const float e0 = fast_exp2(v0[u] - M), e1 = fast_exp2(v1[u] - M);
-        const float inv = 1.f / wave_sum(e0 + e1);
-        acc0 += e0 * inv;
-        acc1 += e1 * inv;
-      }
-    }
-    part[wave][lane] = acc0;
-    part[wave][lane + 64] = acc1;
+    if (a.F_tot <= 24)
+      accumulate_masses<24>(base, a.n_s, a.F_tot, a.F_h, part, tid, lane, wave);
+    else
+      accumulate_masses<72>(base, a.n_s, a.F_tot, a.F_h, part, tid, lane, wave);
     __syncthreads();
     if (wave == 0) {
       float score = -INFINITY;
