@@ -120,20 +120,21 @@ __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
 // ---------------------------------------------------------------------------
 // K / V tiles in LDS: KT rows (keys) x 128 bf16 (256 B per row), row-major.
 // The 16-byte chunk c of row j sits at chunk position c ^ swz(j) with
-// swz(j) = ((j & 3) << 1) | ((j >> 2) & 1) | (j & 8).  For 32 banks (8 lanes
-// of 16 bytes per pass) as for 64 banks (16 lanes per pass) this keeps three
-// access patterns free of bank conflicts:
+// swz(j) = ((j & 3) << 2) | ((j >> 2) & 3).  With 64 banks of 4 bytes this
+// keeps the three access patterns of the tile free of bank conflicts:
 //   - 16 lanes writing the 16 chunks of one row;
-//   - 16 consecutive rows read at one chunk (the K fragments of S^T): every
-//     aligned group of 8 rows lands on 8 distinct positions modulo 8;
-//   - 4 consecutive rows x 2 adjacent chunks (the transposing V reads):
-//     bits 1-2 of swz differ between the 4 rows, so the 8 pieces land on 8
-//     distinct positions modulo 8.
+//   - 16 lanes reading 16 consecutive rows at one chunk (ds_read_b128, the
+//     K fragments of S^T): swz is a permutation of 0..15 over any aligned
+//     16 rows;
+//   - 32 lanes of a transposing read (ds_read_b64_tr_b16, the V^T
+//     fragments) covering 4 aligned consecutive rows x an aligned group of 4
+//     chunks: bits 2-3 of swz take the 4 values over those rows, so the 4
+//     rows' chunk groups fall on disjoint banks.
 template <int KT>
 struct KvTileLds {
   static constexpr int kBytes = KT * 256;
   __device__ static __forceinline__ uint32_t swz(int row) {
-    return (uint32_t)(((row & 3) << 1) | ((row >> 2) & 1) | (row & 8));
+    return (uint32_t)(((row & 3) << 2) | ((row >> 2) & 3));
   }
   __device__ static __forceinline__ uint32_t offset(int row, int chunk) {
     return (uint32_t)(row * 256) + (((uint32_t)chunk ^ swz(row)) << 4);
