@@ -100,7 +100,8 @@ def measure(wname, args, fkv, torch, W):
               "compress": lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
                                                      w.budget_m, L.ckv),
               "attend": lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv, L.out),
-              "dense": lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout)}[args.only]
+              "dense": lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout,
+                                                     L.ckv.attend_ws)}[args.only]
         if args.only == "attend":
             for L in layers:
                 step(L)
@@ -112,7 +113,8 @@ def measure(wname, args, fkv, torch, W):
                             layers, args.steps, args.warmup, torch)
     ms_attend = time_loop(lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv, L.out),
                           layers, args.steps, args.warmup, torch)
-    ms_dense = time_loop(lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout),
+    ms_dense = time_loop(lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout,
+                                                         L.ckv.attend_ws),
                          layers, args.steps, args.warmup, torch)
     kept = base.ckv.kept_tokens
     D = w.head_dim

@@ -155,7 +155,15 @@ fkv_status_t hip_fail(hipError_t e, const char *what) {
 }
 
 fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, const void *v,
-                           const int64_t *tok_off, void *out, void *stream) {
+                           const int64_t *tok_off, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (workspace && d->dtype == FKV_BF16) {
+    const size_t need = fkv::attend_part_bytes();
+    if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
+    if (workspace_bytes < need)
+      return fail(FKV_ERR_WORKSPACE, "attention workspace of %zu bytes, %zu needed",
+                  workspace_bytes, need);
+  }
   fkv::AttendArgs a;
   a.q = q;
   a.k = k;
@@ -169,7 +177,10 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
   a.D = d->head_dim;
   a.c = log2e_scale(*d);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = d->dtype == FKV_BF16 ? fkv::launch_attend_bf16(a, s) : fkv::launch_attend_f32(a, s);
+  a.part = nullptr;
+  a.n_wg = 0;
+  hipError_t e = d->dtype == FKV_BF16 ? fkv::launch_attend_bf16(a, workspace, workspace_bytes, s)
+                                      : fkv::launch_attend_f32(a, s);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return ok();
 }
@@ -280,23 +291,38 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   return ok();
 }
 
+fkv_status_t fkv_attend_workspace(const fkv_desc_t *desc, size_t *workspace_bytes) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!workspace_bytes) return fail(FKV_ERR_NULL, "workspace_bytes is NULL");
+  *workspace_bytes = 0;
+  if (desc->dtype != FKV_BF16) return ok();
+  const size_t need = fkv::attend_part_bytes();
+  if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
+  *workspace_bytes = need;
+  return ok();
+}
+
 fkv_status_t fkv_attend(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv, void *out,
-                        void *stream) {
+                        void *workspace, size_t workspace_bytes, void *stream) {
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;
   if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");
   if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
     return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
-  return attend_common(desc, q, ckv->k, ckv->v, ckv->tok_off, out, stream);
+  return attend_common(desc, q, ckv->k, ckv->v, ckv->tok_off, out, workspace, workspace_bytes,
+                       stream);
 }
 
 fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void *k_cache,
-                              const void *v_cache, void *out, void *stream) {
+                              const void *v_cache, void *out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;
   if (!q || !k_cache || !v_cache || !out)
     return fail(FKV_ERR_NULL, "q, k_cache, v_cache or out is NULL");
-  return attend_common(desc, q, k_cache, v_cache, nullptr, out, stream);
+  return attend_common(desc, q, k_cache, v_cache, nullptr, out, workspace, workspace_bytes,
+                       stream);
 }
 
 const char *fkv_status_str(fkv_status_t status) {

@@ -32,7 +32,7 @@ constexpr int kKT = 64;      // keys per tile
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
 constexpr int kTileBytes = KvTileLds<kKT>::kBytes;
-constexpr float kLazyRescale = 8.0f;         // log2 of the allowed growth (other kernels)
+constexpr int kPartFloats = kBM * kD + 2 * kBM;  // one partial-result slot
 
 struct KvView {
   const __bf16 *k;
@@ -58,6 +58,40 @@ __device__ __forceinline__ KvView kv_view(const AttendArgs &a, int h) {
   return r;
 }
 
+__device__ __forceinline__ int head_tiles(const AttendArgs &a, int h) {
+  const int64_t len = a.tok_off ? a.tok_off[h + 1] - a.tok_off[h] : (int64_t)a.dense_len;
+  return (int)((len + kKT - 1) / kKT);
+}
+
+// Split schedule on XCD x (nb workgroups, nb % 16 == 0, pairs < nb): the
+// XCD's pairs are [p_lo, p_lo + np) and its workgroups xs = 0 .. nb/8 - 1,
+// placed one per CU (xs < nb/16) before any CU takes a second one.  Of two
+// workgroups sharing a CU the older one issues first and runs faster, so
+// when np > nb/16 the first nb/16 workgroups take the first w0 = nb/16
+// pairs whole, and the rest share the remaining R = np - w0 pairs: R main
+// workgroups run tiles [0, split) of one pair each, the ne others the tails
+// [split, tiles) of up to k = ceil(R / ne) pairs each (k = 0: no cut).
+struct XcdSplit {
+  int p_lo, np, w0, ne, k;
+};
+__device__ __forceinline__ XcdSplit xcd_split(int pairs, int nb, int x) {
+  XcdSplit s;
+  s.p_lo = pairs * x / 8;
+  s.np = pairs * (x + 1) / 8 - s.p_lo;
+  s.w0 = s.np > nb / 16 ? nb / 16 : 0;
+  const int r = s.np - s.w0;
+  s.ne = nb / 8 - s.w0 - r;
+  s.k = s.ne > 0 ? (r + s.ne - 1) / s.ne : 0;
+  return s;
+}
+// First tail tile of a pair with nt tiles (nt when nothing is cut).  A
+// tail workgroup runs its k tails one after the other, each restarting the
+// copy pipeline, and takes about 9/8 the time per tile of a main workgroup;
+// split = nt * 9k / (8 + 9k) evens out the two.
+__device__ __forceinline__ int split_tile(int nt, int k) {
+  return k > 0 ? (int)((int64_t)nt * (9 * k) / (8 + 9 * k)) : nt;
+}
+
 __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   // LDS: two K tiles and two V tiles, each its own array.  Step t (parity
   // P = t & 1) reads K(t+1) from sk[1-P] and V(t) from sv[P] while K(t+2) is
@@ -72,39 +106,42 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  // XCD-aware tile order: workgroups are handed to the 8 XCDs round-robin,
-  // so workgroup b runs on XCD b % 8.  Give each XCD a contiguous range of
-  // (head, query tile) pairs so that the workgroups sharing an L2 stream the
-  // same head's K/V at the same time.
-  const int ntq = (a.n_q + kBM - 1) / kBM;
-  int h, qt;
-  {
-    const int nb = gridDim.x, b = blockIdx.x;
-    const int x = b & 7, slot = b >> 3;
-    const int pair = x * (nb >> 3) + min(x, nb & 7) + slot;
-    h = pair / ntq;
-    qt = pair - h * ntq;
-  }
-  const int qi = qt * kBM + wave * 32 + col;
-  const KvView kv = kv_view(a, h);
-  const int64_t rs_bytes = kv.rs * 2;
-
-  // Q^T fragments (B operand of S^T = K Q^T): query qi, dims 16*st + 8*g ..
-  bf16x8 qf[8];
-  if (qi < a.n_q) {
-    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)qi * a.H + h) * kD + 8 * g;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
-  } else {
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
-  }
-
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m = kNegBig, l = 0.f;
   const float c = a.c;
+  const int ntq = (a.n_q + kBM - 1) / kBM;
+  const int pairs = ntq * a.H;
+  // Work: (head, 128-query tile) pairs, p = h * ntq + qt, pair p holding the
+  // tiles(h) key tiles of its head.  Workgroups are handed to the 8 XCDs
+  // round-robin (workgroup b runs on XCD b % 8); each XCD takes a contiguous
+  // run of pairs, so the workgroups sharing an L2 stream the same head's K/V
+  // at the same time.
+  //  - Without a partial-result buffer: one whole pair per workgroup.
+  //  - With one (fewer pairs than workgroups, all resident): the split
+  //    schedule of xcd_split; a pair cut into a main part and a tail leaves
+  //    two partial results for the combine kernel.
+  const int nb = gridDim.x, x = blockIdx.x & 7, xs = blockIdx.x >> 3;
+  int p0, n_items, k = 0, tail = 0;
+  if (!a.part) {
+    p0 = x * (nb >> 3) + min(x, nb & 7) + xs;
+    n_items = 1;
+  } else {
+    const XcdSplit sp = xcd_split(pairs, nb, x);
+    const int r = sp.np - sp.w0;
+    if (xs < sp.w0) {
+      p0 = sp.p_lo + xs;
+      n_items = 1;
+    } else if (xs < sp.w0 + r) {
+      p0 = sp.p_lo + xs;
+      n_items = 1;
+      k = sp.k;
+    } else {
+      const int e = xs - sp.w0 - r;
+      p0 = sp.p_lo + sp.w0 + e * r / sp.ne;
+      n_items = sp.p_lo + sp.w0 + (e + 1) * r / sp.ne - p0;
+      k = sp.k;
+      tail = 1;
+    }
+  }
+  const int64_t rs_bytes = (a.tok_off ? (int64_t)kD : a.kv_row_stride) * 2;
 
   // Staging: wave w fills tile rows 16 w .. 16 w + 15, four rows per
   // instruction; lane i lands at row 16 w + 4 j + i/16, chunk position i%16,
@@ -114,20 +151,17 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   // is a scalar, the lane offsets fixed.
   const int lrow = lane >> 4, lpos = lane & 15;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t range_bytes = (uint32_t)((int64_t)(kv.len - 1) * rs_bytes + kD * 2);
-  const buf_rsrc krsrc = make_rsrc(kv.k, range_bytes);
-  const buf_rsrc vrsrc = make_rsrc(kv.v, range_bytes);
+  // goff[j] carries -j KiB for the copy's immediate offset (row 16 w + 4 j
+  // starts at least j KiB into the tile, so it stays non-negative).
   uint32_t goff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * wave + 4 * j + lrow;
-    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4);
+    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4) - 1024u * j;
   }
   auto issue = [&](const buf_rsrc &rsrc, int it, char *dst) {
     const uint32_t soff = (uint32_t)((int64_t)it * kKT * rs_bytes);
-    char *dw = dst + wave_s * (16 * 256);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) buffer_load_lds16(rsrc, goff[j], soff, dw + j * 1024);
+    buffer_load_lds16x4(rsrc, goff, soff, dst + wave_s * (16 * 256));
   };
 
   // V^T fragment addresses for the transposing reads (tile-relative): lane
@@ -149,6 +183,35 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) kbase[st] = Lds::offset(col, 2 * st + g);
 
+  for (int item = 0; item < n_items; ++item) {
+  const int p = p0 + item;
+  const int h = p / ntq, qt = p - h * ntq;
+  const int nt = head_tiles(a, h);
+  const int ts = split_tile(nt, k);
+  const int t0 = tail ? ts : 0, t1 = tail ? nt : ts;
+  if (t0 >= t1) continue;
+  const int qi = qt * kBM + wave * 32 + col;
+  const KvView kv = kv_view(a, h);
+  const uint32_t range_bytes = (uint32_t)((int64_t)(kv.len - 1) * rs_bytes + kD * 2);
+  const buf_rsrc krsrc = make_rsrc(kv.k, range_bytes);
+  const buf_rsrc vrsrc = make_rsrc(kv.v, range_bytes);
+
+  // Q^T fragments (B operand of S^T = K Q^T): query qi, dims 16*st + 8*g ..
+  bf16x8 qf[8];
+  if (qi < a.n_q) {
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)qi * a.H + h) * kD + 8 * g;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m = kNegBig, l = 0.f;
+
   // S^T = K Q^T for one 64-key tile: 16 fragment reads feed 16 MFMAs on two
   // independent accumulators.
   auto qk = [&](const char *kl, f32x16 *sacc) {
@@ -162,7 +225,6 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
       sacc[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf[i]), qf[i >> 1], sacc[i & 1]);
   };
 
-  const int ntiles = (kv.len + kKT - 1) / kKT;
   // One tile step: softmax of this tile's scores `sc` (computed one step
   // earlier), next tile's scores into `sn`, then O += P V for this tile.
   // `par` is the step's parity as a compile-time constant.
@@ -174,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     char *const v_fill = P ? sv0 : sv1;     // V(it+1)
     wait_vmcnt0();   // K(it+1) and V(it), issued one step ago
     lds_barrier();
-    if (it + 2 < ntiles) issue(krsrc, it + 2, k_fill);
-    if (it + 1 < ntiles) issue(vrsrc, it + 1, v_fill);
+    if (it + 2 < t1) issue(krsrc, it + 2, k_fill);
+    if (it + 1 < t1) issue(vrsrc, it + 1, v_fill);
     const int valid = kv.len - it * kKT;
     if (valid < kKT) {  // ragged last tile: keys past the end get no weight
 #pragma unroll
@@ -221,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     // tile's weights sum past 2^64 (or overflow).  Any common reference gives
     // the same O / l, so skipping the per-tile maximum changes nothing
     // exactly, and weights up to 2^64 are far from fp32 / bf16 overflow.
-    if (it == 0) m = tile_max();
+    if (it == t0) m = tile_max();
 
     // Next tile's scores (independent of this tile's softmax).  On the last
     // step this reads a stale buffer and the result is never used; it stays
@@ -276,37 +338,110 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
-  issue(krsrc, 0, sk0);
-  issue(vrsrc, 0, sv0);
-  if (ntiles > 1) issue(krsrc, 1, sk1);
+  issue(krsrc, t0, sk0);
+  issue(vrsrc, t0, sv0);
+  if (t0 + 1 < t1) issue(krsrc, t0 + 1, sk1);
   wait_vmcnt0();
   lds_barrier();
   f32x16 sa[2], sb[2];
   qk(sk0, sa);
-  // Two steps per trip: the parity is static and the two score buffers swap
-  // roles without copies.
-  int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
+  // Two steps per trip: the parity (counted from t0) is static and the two
+  // score buffers swap roles without copies.
+  int it = t0;
+  for (; it + 1 < t1; it += 2) {
     step(std::integral_constant<int, 0>{}, it, sa, sb);
     step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
   }
-  if (it < ntiles) step(std::integral_constant<int, 0>{}, it, sa, sb);
+  if (it < t1) step(std::integral_constant<int, 0>{}, it, sa, sb);
 
-  const float lt = pair_sum(l);
-  const float inv = 1.f / lt;
-  if (qi < a.n_q) {
-    __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
+  if (t0 == 0 && t1 == nt) {
+    // Whole pair: normalise and store.
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
+    if (qi < a.n_q) {
+      __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = db * 32 + 8 * rr + 4 * g;
+          bf16x2 lo = pack_bf16(o[db][4 * rr] * inv, o[db][4 * rr + 1] * inv);
+          bf16x2 hi2 = pack_bf16(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
+          u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi2)};
+          *reinterpret_cast<u32x2 *>(op + d0) = w;
+        }
+      }
+    }
+  } else {
+    // Part of a pair: partial results into slot 2 p (main part) or
+    // 2 p + 1 (tail).
+    float *slot = a.part + (int64_t)(2 * p + tail) * kPartFloats;
+    const int ql = wave * 32 + col;
+    const float lt = pair_sum(l);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = db * 32 + 8 * rr + 4 * g;
-        bf16x2 lo = pack_bf16(o[db][4 * rr] * inv, o[db][4 * rr + 1] * inv);
-        bf16x2 hi = pack_bf16(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
-        u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<u32x2 *>(op + d0) = w;
+        f32x4 w = {o[db][4 * rr], o[db][4 * rr + 1], o[db][4 * rr + 2], o[db][4 * rr + 3]};
+        *reinterpret_cast<f32x4 *>(slot + ql * kD + d0) = w;
       }
+    if (g == 0) {
+      slot[kBM * kD + ql] = m;
+      slot[kBM * kD + kBM + ql] = lt;
     }
+  }
+
+  // The next item refills the LDS tiles: every wave must be done with
+  // this one's.
+  lds_barrier();
+  }
+}
+
+// Merge of the two halves of every cut pair (block p: pair p):
+// O = sum_s O_s 2^(m_s - M), l = sum_s l_s 2^(m_s - M), M = max_s m_s,
+// out = O / l.  Thread t: query t / 2 of the tile, dims 64 (t & 1) .. +63.
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
+  const int p = blockIdx.x;
+  const int ntq = (a.n_q + kBM - 1) / kBM;
+  const int pairs = ntq * a.H;
+  int x = 0;
+  while (x < 7 && p >= pairs * (x + 1) / 8) ++x;
+  const XcdSplit sp = xcd_split(pairs, a.n_wg, x);
+  if (p - sp.p_lo < sp.w0) return;  // written whole
+  const int h = p / ntq, qt = p - h * ntq;
+  const int nt = head_tiles(a, h);
+  const int ts = split_tile(nt, sp.k);
+  if (ts == 0 || ts == nt) return;  // written whole by one workgroup
+
+  const int t = threadIdx.x, ql = t >> 1, d0 = (t & 1) * 64;
+  const float *s0 = a.part + (int64_t)(2 * p) * kPartFloats;
+  const float *s1 = s0 + kPartFloats;
+  const float m0 = s0[kBM * kD + ql], m1 = s1[kBM * kD + ql];
+  const float M = fmaxf(m0, m1);
+  const float f0 = fast_exp2(m0 - M), f1 = fast_exp2(m1 - M);
+  const float L = s0[kBM * kD + kBM + ql] * f0 + s1[kBM * kD + kBM + ql] * f1;
+  const f32x4 *x0 = reinterpret_cast<const f32x4 *>(s0 + ql * kD + d0);
+  const f32x4 *x1 = reinterpret_cast<const f32x4 *>(s1 + ql * kD + d0);
+  float acc[64];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const f32x4 u = x0[jj], v = x1[jj];
+    acc[4 * jj] = u[0] * f0 + v[0] * f1;
+    acc[4 * jj + 1] = u[1] * f0 + v[1] * f1;
+    acc[4 * jj + 2] = u[2] * f0 + v[2] * f1;
+    acc[4 * jj + 3] = u[3] * f0 + v[3] * f1;
+  }
+  const int qi = qt * kBM + ql;
+  if (qi >= a.n_q) return;
+  const float inv = 1.f / L;
+  __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD + d0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    bf16x2 lo = pack_bf16(acc[j] * inv, acc[j + 1] * inv);
+    bf16x2 hi2 = pack_bf16(acc[j + 2] * inv, acc[j + 3] * inv);
+    u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi2)};
+    *reinterpret_cast<u32x2 *>(op + j) = w;
   }
 }
 
@@ -376,10 +511,39 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
 
 }  // namespace
 
-hipError_t launch_attend_bf16(const AttendArgs &a, hipStream_t s) {
-  if (a.D != kD) return hipErrorInvalidValue;
-  dim3 grid(((a.n_q + kBM - 1) / kBM) * a.H);
-  hipLaunchKernelGGL(attend_bf16_kernel, grid, dim3(256), 0, s, a);
+namespace {
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  return cus;
+}
+}  // namespace
+
+size_t attend_part_bytes() {
+  return (size_t)2 * 2 * device_cus() * kPartFloats * sizeof(float);
+}
+
+hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_bytes,
+                              hipStream_t s) {
+  if (a0.D != kD) return hipErrorInvalidValue;
+  AttendArgs a = a0;
+  const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
+  // Two workgroups fit on a CU (64 KiB of LDS each).  The split schedule
+  // runs exactly that many, all resident at once, when there are fewer
+  // pairs; with more, whole pairs are dealt out as workgroups finish.
+  const int nb = 2 * device_cus();
+  a.part = nullptr;
+  a.n_wg = pairs;
+  if (part && nb > 0 && nb % 16 == 0 && pairs < nb &&
+      part_bytes >= (size_t)2 * nb * kPartFloats * sizeof(float)) {
+    a.part = static_cast<float *>(part);
+    a.n_wg = nb;
+  }
+  hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
+  if (a.part) hipLaunchKernelGGL(attend_combine_kernel, dim3(pairs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

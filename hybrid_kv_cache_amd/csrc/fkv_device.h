@@ -95,12 +95,28 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) 
 }
 
 // 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes
-// at rsrc + soffset + voffset land at lds_wave_base + 16 i.  lds_wave_base
+// at rsrc + soffset + voffset + IMM land at lds_wave_base + IMM + 16 i (the
+// instruction's immediate offset applies to both addresses).  lds_wave_base
 // must be wave-uniform and 1 KiB aligned.  Out-of-range lanes write zeros.
+// Several copies sharing one LDS base and differing by IMM need one M0 value.
+template <int IMM = 0>
 __device__ __forceinline__ void buffer_load_lds16(buf_rsrc rsrc, uint32_t voffset,
                                                   uint32_t soffset, void *lds_wave_base) {
+  static_assert(IMM >= 0 && IMM < 4096, "12-bit immediate offset");
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voffset, soffset, 0, 0);
+      rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voffset, soffset, IMM,
+      0);
+}
+
+// Four 16-byte copies into 4 consecutive KiB of LDS (one wave's 16 tile
+// rows): voff[j] already has j KiB subtracted, so the immediate offsets
+// 0, 1, 2, 3 KiB restore the global address and place the LDS rows.
+__device__ __forceinline__ void buffer_load_lds16x4(buf_rsrc rsrc, const uint32_t *voff,
+                                                    uint32_t soffset, void *lds_wave_base) {
+  buffer_load_lds16<0>(rsrc, voff[0], soffset, lds_wave_base);
+  buffer_load_lds16<1024>(rsrc, voff[1], soffset, lds_wave_base);
+  buffer_load_lds16<2048>(rsrc, voff[2], soffset, lds_wave_base);
+  buffer_load_lds16<3072>(rsrc, voff[3], soffset, lds_wave_base);
 }
 
 // 16-byte global -> LDS copy without a register round trip

@@ -71,13 +71,19 @@ struct AttendArgs {
   int32_t dense_len;      // window length when tok_off is null
   int32_t n_q, H, D;
   float c;                // scale * log2(e)
+  float *part;            // partial-result slots (balanced bf16 schedule) or null
+  int32_t n_wg;           // workgroups of the balanced schedule
 };
 
 hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int total_slots, hipStream_t s);
-hipError_t launch_attend_bf16(const AttendArgs &a, hipStream_t s);
+// Bytes of partial-result buffer that the balanced bf16 attention schedule
+// needs on the current device (2 slots per workgroup, 2 workgroups per CU).
+size_t attend_part_bytes();
+// part / part_bytes: null / 0 for one workgroup per (head, query tile).
+hipError_t launch_attend_bf16(const AttendArgs &a, void *part, size_t part_bytes, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s);
 
 }  // namespace fkv

@@ -79,18 +79,18 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   // past the frame read as zeros (and are masked out of the sums).
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const buf_rsrc krsrc = make_rsrc(kframe, (uint32_t)((int64_t)(len - 1) * rs_bytes + kD * 2));
+  // goff[j] carries -j KiB for the copy's immediate offset (row 16 w + 4 j
+  // starts at least j KiB into the tile).
   uint32_t goff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * wave + 4 * j + lrow;
-    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4);
+    goff[j] = (uint32_t)row * (uint32_t)rs_bytes + ((lpos ^ Lds::swz(row)) << 4) - 1024u * j;
   }
   auto issue = [&](int it) -> bool {
     if (it >= ntiles) return false;
     const uint32_t soff = (uint32_t)((int64_t)it * kKT * rs_bytes);
-    char *dw = ring(it) + wave_s * (16 * 256);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) buffer_load_lds16(krsrc, goff[j], soff, dw + j * 1024);
+    buffer_load_lds16x4(krsrc, goff, soff, ring(it) + wave_s * (16 * 256));
     return true;
   };
   uint32_t kbase[8];

@@ -24,8 +24,8 @@ FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
 FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
-EXPORTED = ("fkv_plan", "fkv_compress", "fkv_attend", "fkv_attend_dense",
-            "fkv_status_str", "fkv_last_error")
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_attend_workspace", "fkv_attend",
+            "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
 
 
 class FkvDesc(ctypes.Structure):
@@ -64,9 +64,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(SZ)]
     lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                  ctypes.POINTER(FkvCkv), P, SZ, P]
-    lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P]
-    lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P]
-    for name in ("fkv_plan", "fkv_compress", "fkv_attend", "fkv_attend_dense"):
+    lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
+    lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
+    lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
+    for name in ("fkv_plan", "fkv_compress", "fkv_attend_workspace", "fkv_attend",
+                 "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fkv_status_str.argtypes = [ctypes.c_int]
     lib.fkv_status_str.restype = ctypes.c_char_p
@@ -141,6 +143,8 @@ class CompressedKV:
                           if with_scores else None)
         self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8,
                                      device=device)
+        # Attention workspace (balanced schedule); None where it is not used.
+        self.attend_ws = attend_workspace(desc, device)
 
     def struct(self) -> FkvCkv:
         return FkvCkv(_ptr(self.k), _ptr(self.v), _ptr(self.tok_off), _ptr(self.seg_idx),
@@ -159,17 +163,44 @@ def fkv_compress(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask
                             ckv.workspace_bytes, _stream(stream)))
 
 
-def fkv_attend(desc: FkvDesc, q, ckv: CompressedKV, out, stream=None) -> None:
+def fkv_attend_workspace(desc: FkvDesc) -> int:
+    """Bytes of the optional attention workspace on the current device."""
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.fkv_attend_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def attend_workspace(desc: FkvDesc, device="cuda"):
+    """A device buffer of fkv_attend_workspace(desc) bytes, or None if 0."""
+    import torch
+    n = fkv_attend_workspace(desc)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def fkv_attend(desc: FkvDesc, q, ckv: CompressedKV, out, workspace="ckv",
+               stream=None) -> None:
+    """workspace: "ckv" (the one CompressedKV allocated), None (one workgroup
+    per head and query tile) or a device buffer."""
     lib = load()
     s = ckv.struct()
-    _check(lib.fkv_attend(ctypes.byref(desc), _ptr(q), ctypes.byref(s), _ptr(out),
+    ws, ws_bytes = _ws(ckv.attend_ws if isinstance(workspace, str) else workspace)
+    _check(lib.fkv_attend(ctypes.byref(desc), _ptr(q), ctypes.byref(s), _ptr(out), ws, ws_bytes,
                           _stream(stream)))
 
 
-def fkv_attend_dense(desc: FkvDesc, q, k_cache, v_cache, out, stream=None) -> None:
+def fkv_attend_dense(desc: FkvDesc, q, k_cache, v_cache, out, workspace=None,
+                     stream=None) -> None:
     lib = load()
+    ws, ws_bytes = _ws(workspace)
     _check(lib.fkv_attend_dense(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                _ptr(out), _stream(stream)))
+                                _ptr(out), ws, ws_bytes, _stream(stream)))
 
 
 def fkv_status_str(status: int) -> str:

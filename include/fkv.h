@@ -117,18 +117,31 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
                           const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* Bytes of the optional attention workspace for the current HIP device: the
+ * bf16 attention can then split its work into equal parts, one per resident
+ * workgroup (two per compute unit), whatever the number of (head, 128-query)
+ * tiles, and merges the pieces of tiles that the split cuts through partial
+ * results kept in the workspace.  0 for fp32.  FKV_ERR_HIP when no device is
+ * visible. */
+fkv_status_t fkv_attend_workspace(const fkv_desc_t *desc, size_t *workspace_bytes);
+
 /* Attention of the whole query block over the compressed cache ([S]
  * 输出与工程收益): out[i, h] = sum_j softmax_j(scale * q[i,h].k_j) v_j over
  * head h's compressed rows, non-causal, fp32 accumulation, result rounded to
  * the element type.  ckv must hold what fkv_compress wrote (only k, v and
- * tok_off are read). */
+ * tok_off are read).  workspace: NULL (one workgroup per head and 128-query
+ * tile) or device memory of at least fkv_attend_workspace's figure, else
+ * FKV_ERR_WORKSPACE; its contents on entry do not matter, and calls that
+ * share one workspace must be ordered (same stream). */
 fkv_status_t fkv_attend(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
-                        void *out, void *stream);
+                        void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Full-KV baseline: the same attention kernel over the whole uncompressed
- * window (every query sees all N_win keys of its head). */
+ * window (every query sees all N_win keys of its head).  workspace as for
+ * fkv_attend. */
 fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void *k_cache,
-                              const void *v_cache, void *out, void *stream);
+                              const void *v_cache, void *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *fkv_status_str(fkv_status_t status);

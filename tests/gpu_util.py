@@ -54,22 +54,24 @@ def run_compress(w, inp, budget_m=None, mask=None, role=None, q=None, k=None, v=
     return desc, ckv, (q, k, v), res
 
 
-def run_attend(desc, q, ckv, n_q, H, D, dtype):
+def run_attend(desc, q, ckv, n_q, H, D, dtype, workspace="ckv"):
     import torch
     out = torch.empty((n_q, H, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
                       device="cuda")
-    announce(f"fkv_attend Nq={n_q} H={H} D={D} kept={ckv.kept_tokens}")
-    fkv.fkv_attend(desc, q, ckv, out)
+    mode = "per-pair" if workspace is None else "balanced"
+    announce(f"fkv_attend Nq={n_q} H={H} D={D} kept={ckv.kept_tokens} {mode}")
+    fkv.fkv_attend(desc, q, ckv, out, workspace)
     torch.cuda.synchronize()
     return out
 
 
-def run_attend_dense(desc, q, k, v, n_q, H, D, dtype):
+def run_attend_dense(desc, q, k, v, n_q, H, D, dtype, workspace=None):
     import torch
     out = torch.empty((n_q, H, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
                       device="cuda")
-    announce(f"fkv_attend_dense Nq={n_q} H={H} D={D}")
-    fkv.fkv_attend_dense(desc, q, k, v, out)
+    mode = "per-pair" if workspace is None else "balanced"
+    announce(f"fkv_attend_dense Nq={n_q} H={H} D={D} {mode}")
+    fkv.fkv_attend_dense(desc, q, k, v, out, workspace)
     torch.cuda.synchronize()
     return out
 

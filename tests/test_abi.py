@@ -167,9 +167,26 @@ def _capture_error(d, cap, ws):
 def test_attend_argument_errors(lib):
     d = fkv.make_desc(2, 128, 16, 4, 3, 4)
     ckv = fkv.FkvCkv(None, None, None, None, None, None, 0)
-    assert lib.fkv_attend(ctypes.byref(d), 0x1000, ctypes.byref(ckv), 0x1000, None) == \
-        fkv.FKV_ERR_NULL
-    assert lib.fkv_attend_dense(ctypes.byref(d), 0x1000, None, 0x1000, 0x1000, None) == \
-        fkv.FKV_ERR_NULL
+    assert lib.fkv_attend(ctypes.byref(d), 0x1000, ctypes.byref(ckv), 0x1000, None, 0,
+                          None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_attend_dense(ctypes.byref(d), 0x1000, None, 0x1000, 0x1000, None, 0,
+                                None) == fkv.FKV_ERR_NULL
     d.dtype = 5
-    assert lib.fkv_attend_dense(ctypes.byref(d), 1, 1, 1, 1, None) == fkv.FKV_ERR_DTYPE
+    assert lib.fkv_attend_dense(ctypes.byref(d), 1, 1, 1, 1, None, 0, None) == fkv.FKV_ERR_DTYPE
+
+
+def test_attend_workspace_query(lib):
+    """The workspace figure: NULL output rejected, bad descriptors rejected,
+    0 for fp32 (no balanced schedule there), and for bf16 either a positive
+    figure (a device is visible) or FKV_ERR_HIP (none is)."""
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    assert lib.fkv_attend_workspace(ctypes.byref(d), None) == fkv.FKV_ERR_NULL
+    n = ctypes.c_size_t(123)
+    st = lib.fkv_attend_workspace(ctypes.byref(d), ctypes.byref(n))
+    assert (st == fkv.FKV_OK and n.value > 0) or (st == fkv.FKV_ERR_HIP and n.value == 0)
+    f = fkv.make_desc(2, 64, 16, 4, 3, 4, dtype="f32")
+    n = ctypes.c_size_t(123)
+    assert lib.fkv_attend_workspace(ctypes.byref(f), ctypes.byref(n)) == fkv.FKV_OK
+    assert n.value == 0
+    d.head_dim = 96
+    assert lib.fkv_attend_workspace(ctypes.byref(d), ctypes.byref(n)) == fkv.FKV_ERR_DTYPE

@@ -34,8 +34,13 @@ def full_case(w, inp, budget_m=None, mask=None, role=None, check_dense=True):
     out = G.run_attend(desc, q, ckv, w.n_q, w.num_heads, w.head_dim, w.dtype)
     ref = O.attend(inp.q, k_c, v_c, tok_off)
     errs = G.check_output(G.host_f64(out), ref, w.dtype)
+    if ckv.attend_ws is not None:
+        # the other schedule: one workgroup per (head, query tile)
+        out1 = G.run_attend(desc, q, ckv, w.n_q, w.num_heads, w.head_dim, w.dtype, None)
+        G.check_output(G.host_f64(out1), ref, w.dtype)
     if check_dense:
-        dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype)
+        dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype,
+                                  ckv.attend_ws)
         G.check_output(G.host_f64(dout), O.attend_dense(inp.q, inp.k, inp.v), w.dtype)
     return desc, ckv, (q, k, v), out, kept, errs
 
@@ -72,8 +77,13 @@ def test_keep_all_equals_dense_bitwise():
     desc, ckv, (q, k, v), out, kept, _ = full_case(w, inp, budget_m=6, mask=mask,
                                                    check_dense=False)
     assert all(list(kh) == list(range(6)) for kh in kept)
-    dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype)
+    # same schedule on both sides (the balanced one, where there is one)
+    dout = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype,
+                              ckv.attend_ws)
     assert np.array_equal(fkv.to_host(out), fkv.to_host(dout))
+    out1 = G.run_attend(desc, q, ckv, w.n_q, w.num_heads, w.head_dim, w.dtype, None)
+    dout1 = G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim, w.dtype, None)
+    assert np.array_equal(fkv.to_host(out1), fkv.to_host(dout1))
 
 
 def test_budget_above_history_keeps_all():
@@ -160,3 +170,52 @@ def test_late_frames_with_much_larger_scores():
         else:
             inp.k = k.astype(np.float32)
         full_case(w, inp)
+
+
+@pytest.mark.parametrize("T,H,Fh,Fc,seed", [
+    (10, 1, 2, 1, 31),     # one pair of one tile: not cut (the tail takes it whole)
+    (100, 1, 3, 1, 36),    # one pair of 7 tiles: cut in halves
+    (300, 1, 40, 2, 32),   # 5 pairs x 197 tiles, one tail workgroup per pair
+    (257, 7, 9, 3, 33),    # 49 pairs x 49 tiles
+    (1560, 12, 18, 3, 34), # 480P window: 444 pairs x 512 tiles, up to 7 tails each
+])
+def test_split_schedule(T, H, Fh, Fc, seed):
+    """With a workspace and fewer (head, query tile) pairs than resident
+    workgroups, attention cuts pairs into a main part and a tail run by
+    different workgroups and merges the two partial results: the result
+    matches the oracle and the one-workgroup-per-pair schedule."""
+    w = W.small_workload(tokens_per_frame=T, num_heads=H, hist_frames=Fh, cur_frames=Fc,
+                         budget_m=min(3, Fh), num_static=0, query_stride=7, seed=seed)
+    inp = W.generate_layer(w)
+    desc = fkv.desc_for(w)
+    q, k, v = (fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v))
+    ws = fkv.attend_workspace(desc)
+    assert ws is not None
+    if w.n_q * w.n_win * H <= 100_000_000:
+        ref = O.attend_dense(inp.q, inp.k, inp.v)
+        rows = None
+    else:  # sampled rows, each computed by the oracle one by one
+        rows = np.random.default_rng(seed).choice(w.n_q, 48, replace=False)
+        ref = O.attend_dense(inp.q, inp.k, inp.v, rows=rows)
+    outs = []
+    for workspace in (ws, None):
+        out = G.run_attend_dense(desc, q, k, v, w.n_q, H, w.head_dim, w.dtype, workspace)
+        got = G.host_f64(out)
+        G.check_output(got if rows is None else got[rows], ref, w.dtype)
+        outs.append(got)
+    # the two schedules differ only by the order of fp32 sums: at most a
+    # couple of bf16 rounding steps apart
+    assert np.max(np.abs(outs[0] - outs[1])) <= 2e-2
+
+
+def test_attend_workspace_too_small_is_rejected():
+    w = W.small_workload(tokens_per_frame=20, num_heads=2, hist_frames=3, seed=35)
+    inp = W.generate_layer(w)
+    desc = fkv.desc_for(w)
+    q, k, v = (fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v))
+    import torch
+    n = fkv.fkv_attend_workspace(desc)
+    small = torch.empty(n - 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="workspace"):
+        fkv.fkv_attend_dense(desc, q, k, v, out, small)
