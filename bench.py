@@ -39,7 +39,11 @@ def parse():
     ap.add_argument("--workload", default="480p_layer")
     ap.add_argument("--secondary", default="1080p_layer",
                     help="second workload to report ('' to skip)")
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=4,
+                    help="device copies of layer 0 that the timed loops cycle over")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="cycle over the workload's first N layers (own seeds, roles and "
+                         "masks) instead of copies of layer 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run the timed loop only (for rocprofv3), print nothing else")
@@ -89,7 +93,12 @@ def measure(wname, args, fkv, torch, W):
     w = W.WORKLOADS[wname]
     inp = W.generate_layer(w, 0)
     base = Layer(w, inp, fkv, torch)
-    layers = [base] + [Layer(w, inp, fkv, torch, src=base) for _ in range(max(args.copies, 1) - 1)]
+    if args.layers > 1:
+        layers = [base] + [Layer(w, W.generate_layer(w, l), fkv, torch)
+                           for l in range(1, min(args.layers, w.num_layers))]
+    else:
+        layers = [base] + [Layer(w, inp, fkv, torch, src=base)
+                           for _ in range(max(args.copies, 1) - 1)]
 
     def step(L):
         fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
@@ -116,57 +125,65 @@ def measure(wname, args, fkv, torch, W):
     ms_dense = time_loop(lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout,
                                                          L.ckv.attend_ws),
                          layers, args.steps, args.warmup, torch)
-    kept = base.ckv.kept_tokens
+    kept = sum(L.ckv.kept_tokens for L in layers) / len(layers)  # mean over the layers
     D = w.head_dim
     attn_flop = 4.0 * w.n_q * D * kept
     dense_flop = 4.0 * w.n_q * D * w.n_win * w.num_heads
     elt = 2 if w.dtype == "bf16" else 4
     return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_compress=ms_compress,
                 ms_attend=ms_attend, ms_dense=ms_dense, attn_flop=attn_flop,
-                dense_flop=dense_flop,
+                dense_flop=dense_flop, n_layers=len(layers),
                 compact_bytes=4.0 * kept * D * elt,
                 kept_frac_hist=(kept / w.num_heads / w.tokens_per_frame - w.cur_frames)
-                / w.hist_frames)
+                / max(w.hist_frames, 1))
 
 
-def cpu_baseline(w, inp, rows_sample):
-    """The oracle as it stands, timed on this host: full scoring, selection
-    and compaction, attention on a seeded sample of query rows, extrapolated
-    linearly in rows to the whole query block."""
+def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
+    """The oracle as it stands, timed on this host over the whole layer
+    (scoring, selection, compaction and attention of every query row),
+    repeated until about min_seconds of work have run (at most max_reps)."""
     from oracle import forcing_kv as O
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    c = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
-                   w.tokens_per_frame, w.hist_frames, w.cur_frames, w.query_stride)
-    t1 = time.perf_counter()
-    rows = np.sort(np.random.default_rng(0).choice(w.n_q, rows_sample, replace=False))
-    O.attend(inp.q, c["k_c"], c["v_c"], c["tok_off"], rows=rows)
-    t2 = time.perf_counter()
-    t_layer = (t1 - t0) + (t2 - t1) * (w.n_q / rows_sample)
-    return {"value": w.n_q / t_layer, "unit": "query tok/s per layer", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{w.name}: full compress (score+select+compact, {t1 - t0:.1f} s) + "
-                      f"attention of {rows_sample}/{w.n_q} query rows ({t2 - t1:.1f} s), "
-                      f"attention time scaled by {w.n_q / rows_sample:.2f}; float64 NumPy"}
+    t_comp = t_attn = 0.0
+    reps = 0
+    while reps < max_reps and (t_comp + t_attn) < min_seconds:
+        t0 = time.perf_counter()
+        c = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                       w.tokens_per_frame, w.hist_frames, w.cur_frames, w.query_stride)
+        t1 = time.perf_counter()
+        O.attend(inp.q, c["k_c"], c["v_c"], c["tok_off"])
+        t2 = time.perf_counter()
+        t_comp += t1 - t0
+        t_attn += t2 - t1
+        reps += 1
+    return {"value": reps * w.n_q / (t_comp + t_attn), "unit": "query tok/s per layer",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: {reps} full layer pass(es), all {w.n_q} query rows: "
+                      f"compress (score+select+compact) {t_comp:.1f} s + attention "
+                      f"{t_attn:.1f} s; float64 NumPy"}
 
 
-def traffic_record(kernel: str):
+def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
+    taken on this workload and on the current kernel source."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         import hashlib
         rec = json.load(open(path)).get(kernel)
-        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_kv_cache_amd",
-                           "csrc", rec["source"])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        return rec["bytes_per_launch"] if digest == rec["sha256"] else None
+        if rec["workload"] != workload:
+            return None
+        csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_kv_cache_amd",
+                            "csrc")
+        h = hashlib.sha256()
+        for name in rec["sources"]:
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        return rec["bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
     except Exception:
         return None
 
@@ -215,10 +232,13 @@ def main():
         "config": {"workload": w.name, "heads": w.num_heads, "head_dim": w.head_dim,
                    "tokens_per_frame": w.tokens_per_frame, "hist_frames": w.hist_frames,
                    "cur_frames": w.cur_frames, "query_tokens": w.n_q, "budget_m": w.budget_m,
-                   "query_stride": w.query_stride, "layer_copies": args.copies},
-        "roofline": {"bound": "mfma", "kernel": "attend_bf16 (fkv_attend)",
+                   "query_stride": w.query_stride,
+                   **({"layers": r["n_layers"]} if args.layers > 1
+                      else {"layer_copies": r["n_layers"]})},
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                     "kernel": f"attend_{w.dtype} (fkv_attend)",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": attn_tflops / peak, "traffic": traffic_record("attend")},
+                     "frac": attn_tflops / peak, "traffic": traffic_record("attend", w.name)},
         "breakdown_ms": {"compress": r["ms_compress"], "attend": r["ms_attend"],
                          "attend_dense": r["ms_dense"]},
         "speedup_vs_full_kv": r["ms_dense"] / r["ms_step"],
@@ -241,7 +261,7 @@ def main():
         }
         del r2
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, r["inp"], rows_sample=max(1, w.n_q // 4))
+        line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
