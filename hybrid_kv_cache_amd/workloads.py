@@ -205,6 +205,79 @@ def generate_layer(w: Workload, layer: int = 0, *, zero_q: bool = False) -> Laye
     return out
 
 
+@dataclasses.dataclass
+class RolloutInputs:
+    """Inputs of n_chunks consecutive chunk steps of one layer.  Frame store
+    k / v [(F_h + n_chunks F_c) T, H, D] token-major: chunk 0's window is
+    frames [0, F_h + F_c), chunk c's current frames are
+    [F_h + c F_c, F_h + (c + 1) F_c).  q[c] [Nq, H, D] are chunk c's queries.
+    Same value conventions as LayerInputs."""
+    workload: Workload
+    n_chunks: int
+    q: List[np.ndarray]
+    k: np.ndarray
+    v: np.ndarray
+    head_role: np.ndarray
+    static_keep_mask: np.ndarray   # [H, F_h]: chunk 0's window (frame ids 0 .. F_h - 1)
+
+    def window(self) -> LayerInputs:
+        """Chunk 0 as a plain one-layer window."""
+        w = self.workload
+        n = w.n_win
+        return LayerInputs(workload=w, layer=0, q=self.q[0], k=self.k[:n], v=self.v[:n],
+                           head_role=self.head_role, static_keep_mask=self.static_keep_mask,
+                           target_frame=np.zeros(w.num_heads, dtype=np.int64))
+
+    def current(self, name: str, c: int) -> np.ndarray:
+        """Chunk c's current-frame rows of k or v: [F_c T, H, D]."""
+        w = self.workload
+        lo = (w.hist_frames + c * w.cur_frames) * w.tokens_per_frame
+        return getattr(self, name)[lo:lo + w.cur_frames * w.tokens_per_frame]
+
+
+def generate_rollout(w: Workload, n_chunks: int, seed: Optional[int] = None) -> RolloutInputs:
+    """Drift-plus-Gaussian generator over a longer frame sequence.
+
+    Draw order from Generator(PCG64(seed or the workload's layer-0 seed)):
+      1. head roles as in generate_layer;
+      2. target frame per (chunk, head): uniform over the frames before that
+         chunk's current frames;
+      3. drift over all F_h + n_chunks F_c frames (N(0, 0.3^2) steps);
+      4. keys mu + N(0, 1); 5. values N(0, 1);
+      6. queries of each chunk: N(0, 1) + 0.5 mu[h, target[c, h]].
+    """
+    H, D, T = w.num_heads, w.head_dim, w.tokens_per_frame
+    Fh, Fc = w.hist_frames, w.cur_frames
+    F_all = Fh + n_chunks * Fc
+    rng = np.random.Generator(np.random.PCG64(w.seed(0) if seed is None else seed))
+    role = np.full(H, DYNAMIC, dtype=np.uint8)
+    if w.fixed_static_heads is not None:
+        role[list(w.fixed_static_heads)] = STATIC
+    else:
+        role[rng.permutation(H)[: w.num_static]] = STATIC
+    tgt = np.stack([rng.integers(0, max(Fh + c * Fc, 1), H) for c in range(n_chunks)])
+    mu = np.cumsum(np.float32(0.3) * rng.standard_normal((H, F_all, D), dtype=np.float32),
+                   axis=1, dtype=np.float32)
+    k = rng.standard_normal((H, F_all, T, D), dtype=np.float32)
+    k += mu[:, :, None, :]
+    v = rng.standard_normal((H, F_all * T, D), dtype=np.float32)
+    qs = []
+    for c in range(n_chunks):
+        q = rng.standard_normal((H, w.n_q, D), dtype=np.float32)
+        q += np.float32(0.5) * mu[np.arange(H), tgt[c]][:, None, :]
+        qs.append(q)
+    k = k.reshape(H, F_all * T, D)
+
+    def to_token_major(a):
+        t = np.ascontiguousarray(a.transpose(1, 0, 2))
+        return round_to_bf16_bits(t) if w.dtype == "bf16" else t
+
+    mask = np.tile(chunk_boundary_mask(Fh, Fc), (H, 1))
+    return RolloutInputs(workload=w, n_chunks=n_chunks, q=[to_token_major(q) for q in qs],
+                         k=to_token_major(k), v=to_token_major(v), head_role=role,
+                         static_keep_mask=np.ascontiguousarray(mask, dtype=np.uint8))
+
+
 def iter_layers(w: Workload, layers: Optional[List[int]] = None) -> Iterator[LayerInputs]:
     for l in (range(w.num_layers) if layers is None else layers):
         yield generate_layer(w, l)

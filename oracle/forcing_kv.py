@@ -28,7 +28,8 @@ ranking ties broken by the lower frame index; kept frames in ascending order,
 the current chunk last; non-causal attention with scale 1/sqrt(D)).
 
 Pinned by tests/test_oracle_pins.py (invariants, closed forms, brute force,
-library cross-checks).  Parity of generic numeric outputs is otherwise
+library cross-checks) and, for the rolling cache, tests/test_oracle_rolling.py
+(reduction to the plain window, recomputation from the frame store).  Parity of generic numeric outputs is otherwise
 pinned only through those checks; no page prints a worked example.
 
 Layouts (token-major):  q [Nq, H, D];  k, v [N_win, H, D] with the window's
@@ -248,6 +249,153 @@ def compress(q, k, v, head_role, static_keep_mask, budget_m: int,
                                                   hist_frames, cur_frames)
     return dict(scores=scores, kept=kept, k_c=k_c, v_c=v_c, seg_idx=seg_idx,
                 seg_off=seg_off, tok_off=tok_off)
+
+
+def compress_ragged(q, hist_k, hist_v, hist_tok_off, cur_k, cur_v, head_role,
+                    static_keep_mask, budget_m: int, tokens_per_frame: int,
+                    cur_frames: int, query_stride: int, scale: float = 0.0
+                    ) -> Dict[str, np.ndarray]:
+    """Compression of one layer whose history differs from head to head (a
+    rolling compressed cache, [S] 输出与工程收益: the compressed K/V replace the
+    cache, here also for the next chunk).
+
+    Head h's window is its own history, the T-row frames of rows
+    [hist_tok_off[h], hist_tok_off[h+1]) of hist_k / hist_v (oldest first),
+    followed by the current chunk's frames cur_k[:, h] ([F_c T, H, D]).
+    Scoring, selection and compaction follow compress() head by head, with
+    F_h replaced by the head's own history length n_h: a dynamic head scores
+    its n_h history frames by the mean softmax mass over its whole window and
+    keeps min(m, n_h); a static head keeps the frames its mask row marks among
+    its n_h (mask entries beyond n_h must be 0).  scores [H, F_h max] hold NaN
+    beyond n_h and for static heads.
+    """
+    T = tokens_per_frame
+    qf = as_f64(q)
+    H, D = qf.shape[1], qf.shape[2]
+    sc = logit_scale(D, scale)
+    f_max = static_keep_mask.shape[1]
+    if budget_m < 0:
+        raise ValueError("budget_m must be >= 0")
+    scores = np.full((H, f_max), np.nan, dtype=np.float64)
+    kept = []
+    n_hist = []
+    for h in range(H):
+        lo, hi = int(hist_tok_off[h]), int(hist_tok_off[h + 1])
+        if (hi - lo) % T:
+            raise ValueError("a history range is not a whole number of frames")
+        n_h = (hi - lo) // T
+        if n_h > f_max:
+            raise ValueError("a head's history is longer than the mask rows")
+        n_hist.append(n_h)
+        if head_role[h] == DYNAMIC:
+            if n_h:
+                win = np.concatenate([as_f64(hist_k[lo:hi]), as_f64(cur_k[:, h])], axis=0)
+                mass = frame_masses(qf[:, h, :], win, T, query_stride, sc)
+                scores[h, :n_h] = mass[:, :n_h].mean(axis=0)
+            kept.append(select_dynamic(scores[h, :n_h], budget_m))
+        else:
+            if np.any(np.asarray(static_keep_mask[h, n_h:]) != 0):
+                raise ValueError("static mask marks a frame beyond the head's history")
+            kept.append(select_static(static_keep_mask[h, :n_h]))
+    seg_idx, seg_off, tok_off = offsets(kept, T, cur_frames)
+    k_c = np.empty((int(tok_off[H]), D), dtype=hist_k.dtype)
+    v_c = np.empty((int(tok_off[H]), D), dtype=hist_v.dtype)
+    for h in range(H):
+        lo = int(hist_tok_off[h])
+        row = int(tok_off[h])
+        for f in kept[h]:
+            k_c[row:row + T] = hist_k[lo + f * T:lo + (f + 1) * T]
+            v_c[row:row + T] = hist_v[lo + f * T:lo + (f + 1) * T]
+            row += T
+        for j in range(cur_frames):
+            k_c[row:row + T] = cur_k[j * T:(j + 1) * T, h, :]
+            v_c[row:row + T] = cur_v[j * T:(j + 1) * T, h, :]
+            row += T
+    return dict(scores=scores, kept=kept, n_hist=np.array(n_hist), k_c=k_c, v_c=v_c,
+                seg_idx=seg_idx, seg_off=seg_off, tok_off=tok_off)
+
+
+def refresh_current(k_c, v_c, tok_off, cur_k, cur_v, tokens_per_frame: int,
+                    cur_frames: int):
+    """Selection reused across the denoising steps of one chunk: the kept
+    history rows stay, and the last F_c frames of every head's range (its
+    current chunk) are copied again from the new cur_k / cur_v [F_c T, H, D]."""
+    T = tokens_per_frame
+    k2, v2 = k_c.copy(), v_c.copy()
+    for h in range(len(tok_off) - 1):
+        hi = int(tok_off[h + 1])
+        for j in range(cur_frames):
+            r = hi - (cur_frames - j) * T
+            k2[r:r + T] = cur_k[j * T:(j + 1) * T, h, :]
+            v2[r:r + T] = cur_v[j * T:(j + 1) * T, h, :]
+    return k2, v2
+
+
+def is_chunk_boundary(frame_id: int, cur_frames: int) -> bool:
+    """Frame ids count from 0, chunks are the aligned runs of F_c ids: a
+    frame is a boundary when it is the sink (id 0) or the first or last frame
+    of its chunk ([S] 关键模块 › 1 and 2: static heads attend to chunk start and
+    end positions)."""
+    return frame_id == 0 or frame_id % cur_frames in (0, cur_frames - 1)
+
+
+def roll_static_keep(frame_ids: Sequence[int], cur_frames: int, cap: int) -> np.ndarray:
+    """Static head in a rolling cache: keep the boundary frames of its history
+    (ids as above); while more than cap are kept, drop the oldest kept frame
+    that is not the sink.  Returns a 0/1 mask over frame_ids."""
+    keep = [i for i, fid in enumerate(frame_ids) if is_chunk_boundary(int(fid), cur_frames)]
+    while len(keep) > cap:
+        drop = next((j for j, i in enumerate(keep) if frame_ids[i] != 0), 0)
+        keep.pop(drop)
+    mask = np.zeros(len(frame_ids), dtype=np.uint8)
+    mask[keep] = 1
+    return mask
+
+
+def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray,
+            head_role, budget_m: int, tokens_per_frame: int, hist_frames: int,
+            cur_frames: int, query_stride: int, scale: float = 0.0) -> List[Dict]:
+    """Consecutive chunk steps of one layer with a rolling compressed cache.
+
+    Chunk 0 compresses the plain window (frames [0, F_h + F_c) of the frame
+    store k_all / v_all).  The compressed cache of chunk c - 1 (kept history,
+    then its now finished current chunk) is chunk c's history: frames not kept
+    are gone for good, the finished chunk is appended.  Chunk c's current
+    frames are [F_h + c F_c, F_h + (c + 1) F_c) of the store.  Static heads
+    keep the boundary frames of their history (roll_static_keep, chunk 0
+    included) up to cap = F_h - F_c, so that no history outgrows F_h frames;
+    dynamic heads keep their top m, which must also be at most F_h - F_c.
+    Each result carries the static masks used (``mask`` [H, F_h]) and the
+    absolute frame ids of every head's compacted frames (``ids``).
+    """
+    T, Fh, Fc = tokens_per_frame, hist_frames, cur_frames
+    H = len(head_role)
+    if budget_m > Fh - Fc:
+        raise ValueError("a rolling cache needs m <= F_h - F_c")
+    out = []
+    for c in range(len(q_chunks)):
+        first = Fh + c * Fc
+        prev_ids = [list(range(Fh))] * H if c == 0 else out[-1]["ids"]
+        mask = np.zeros((H, Fh), dtype=np.uint8)
+        for h in range(H):
+            if head_role[h] != DYNAMIC:
+                mk = roll_static_keep(prev_ids[h], Fc, Fh - Fc)
+                mask[h, :len(mk)] = mk
+        if c == 0:
+            n_win = (Fh + Fc) * T
+            r = compress(q_chunks[0], k_all[:n_win], v_all[:n_win], head_role, mask,
+                         budget_m, T, Fh, Fc, query_stride, scale)
+        else:
+            prev = out[-1]
+            cur_k = k_all[first * T:(first + Fc) * T]
+            cur_v = v_all[first * T:(first + Fc) * T]
+            r = compress_ragged(q_chunks[c], prev["k_c"], prev["v_c"], prev["tok_off"], cur_k,
+                                cur_v, head_role, mask, budget_m, T, Fc, query_stride, scale)
+        r["ids"] = [[prev_ids[h][f] for f in r["kept"][h]] + list(range(first, first + Fc))
+                    for h in range(H)]
+        r["mask"] = mask
+        out.append(r)
+    return out
 
 
 def cutoff_band(score_row: np.ndarray, budget_m: int, rel: float = TIE_REL):

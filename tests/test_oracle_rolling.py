@@ -1,0 +1,141 @@
+"""Pins of the oracle's rolling-cache functions (compress_ragged,
+refresh_current, roll_static_keep, rollout) against what the plain-window
+oracle and the frame store fix independently."""
+import numpy as np
+import pytest
+
+from hybrid_kv_cache_amd import workloads as W
+from oracle import forcing_kv as O
+
+
+def _ragged_window(w, inp):
+    """The plain window's history laid out head-major (head h: its F_h frames)."""
+    T, Fh, H = w.tokens_per_frame, w.hist_frames, w.num_heads
+    hk = np.concatenate([inp.k[:Fh * T, h] for h in range(H)], axis=0)
+    hv = np.concatenate([inp.v[:Fh * T, h] for h in range(H)], axis=0)
+    off = np.arange(H + 1, dtype=np.int64) * Fh * T
+    return hk, hv, off
+
+
+@pytest.mark.parametrize("dtype,seed", [("f32", 1), ("bf16", 2)])
+def test_ragged_equals_plain_window(dtype, seed):
+    """With every head's history equal to the plain window's, the ragged
+    compression is the plain one: same scores, kept frames, offsets, rows."""
+    w = W.small_workload(dtype=dtype, head_dim=64 if dtype == "f32" else 128,
+                         tokens_per_frame=12, num_heads=4, hist_frames=6, budget_m=3,
+                         num_static=2, seed=seed)
+    inp = W.generate_layer(w)
+    T, Fh, Fc = w.tokens_per_frame, w.hist_frames, w.cur_frames
+    ref = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                     T, Fh, Fc, w.query_stride)
+    hk, hv, off = _ragged_window(w, inp)
+    cur = slice(Fh * T, (Fh + Fc) * T)
+    got = O.compress_ragged(inp.q, hk, hv, off, inp.k[cur], inp.v[cur], inp.head_role,
+                            inp.static_keep_mask, w.budget_m, T, Fc, w.query_stride)
+    np.testing.assert_allclose(got["scores"], ref["scores"], rtol=1e-13, atol=0)
+    assert all(list(a) == list(b) for a, b in zip(got["kept"], ref["kept"]))
+    for key in ("k_c", "v_c", "seg_idx", "seg_off", "tok_off"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+def test_ragged_rejects_bad_histories():
+    w = W.small_workload(tokens_per_frame=8, num_heads=2, hist_frames=4, seed=3)
+    inp = W.generate_layer(w)
+    hk, hv, off = _ragged_window(w, inp)
+    cur = inp.k[w.hist_frames * 8:]
+    bad = off.copy()
+    bad[1] += 3  # not a whole number of frames
+    with pytest.raises(ValueError):
+        O.compress_ragged(inp.q, hk, hv, bad, cur, cur, inp.head_role, inp.static_keep_mask,
+                          2, 8, w.cur_frames, w.query_stride)
+    mask = np.zeros((2, 8), dtype=np.uint8)
+    mask[:, 6] = 1  # beyond every head's 4 history frames
+    role = np.zeros(2, dtype=np.uint8)
+    with pytest.raises(ValueError):
+        O.compress_ragged(inp.q, hk, hv, off, cur, cur, role, mask, 2, 8, w.cur_frames,
+                          w.query_stride)
+
+
+def test_roll_static_keep_closed_forms():
+    ids = list(range(18))
+    # sink plus first and last frame of each aligned 3-frame chunk
+    assert list(np.flatnonzero(O.roll_static_keep(ids, 3, 15))) == [0, 2, 3, 5, 6, 8, 9, 11,
+                                                                    12, 14, 15, 17]
+    # over the cap: the oldest kept frames other than the sink go first
+    assert list(np.flatnonzero(O.roll_static_keep(ids, 3, 3))) == [0, 15, 17]
+    # the rule matches the plain window's static pattern when F_h is whole chunks
+    assert np.array_equal(O.roll_static_keep(ids, 3, 18), W.chunk_boundary_mask(18, 3))
+    # a history without the sink
+    assert list(np.flatnonzero(O.roll_static_keep([4, 5, 6, 7, 8], 3, 2))) == [2, 4]
+
+
+def test_refresh_current_equals_compaction_of_new_chunk():
+    """Reusing the selection: the refreshed cache equals a compaction of the
+    window with the new current chunk and the same kept frames."""
+    w = W.small_workload(tokens_per_frame=10, num_heads=3, hist_frames=6, seed=4)
+    inp = W.generate_layer(w)
+    T, Fh, Fc = w.tokens_per_frame, w.hist_frames, w.cur_frames
+    res = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                     T, Fh, Fc, w.query_stride)
+    rng = np.random.default_rng(5)
+    k2, v2 = inp.k.copy(), inp.v.copy()
+    k2[Fh * T:] = rng.integers(0, 2 ** 16, k2[Fh * T:].shape, dtype=np.uint16) & 0x7F7F
+    v2[Fh * T:] = rng.integers(0, 2 ** 16, v2[Fh * T:].shape, dtype=np.uint16) & 0x7F7F
+    got_k, got_v = O.refresh_current(res["k_c"], res["v_c"], res["tok_off"], k2[Fh * T:],
+                                     v2[Fh * T:], T, Fc)
+    ref_k, ref_v, _, _, _ = O.compact(k2, v2, res["kept"], T, Fh, Fc)
+    assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)
+
+
+@pytest.mark.parametrize("m,num_static,seed", [(2, 2, 6), (3, 1, 7), (0, 1, 8)])
+def test_rollout_against_frame_store(m, num_static, seed):
+    """Every chunk of a rollout, recomputed from the frame store by frame id:
+    the history a head scores is exactly the frames its ids name (the store
+    rows, not the previous cache, are read here), the scores and kept sets
+    follow, static heads keep the boundary ids, and the cache stops growing."""
+    w = W.small_workload(tokens_per_frame=8, num_heads=4, hist_frames=9, budget_m=m,
+                         num_static=num_static, query_stride=3, seed=seed)
+    n_chunks = 6
+    ro = W.generate_rollout(w, n_chunks)
+    T, Fh, Fc = w.tokens_per_frame, w.hist_frames, w.cur_frames
+    out = O.rollout(ro.q, ro.k, ro.v, ro.head_role, m, T, Fh, Fc, w.query_stride)
+    kf = O.as_f64(ro.k)
+    sc = O.logit_scale(w.head_dim)
+    prev_ids = [list(range(Fh))] * w.num_heads
+    sizes = []
+    for c, r in enumerate(out):
+        first = Fh + c * Fc
+        for h in range(w.num_heads):
+            hist = prev_ids[h]
+            if ro.head_role[h] == O.DYNAMIC:
+                rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in hist]
+                                      + [np.arange(first * T, (first + Fc) * T)])
+                mass = O.frame_masses(O.as_f64(ro.q[c])[:, h], kf[rows, h], T,
+                                      w.query_stride, sc)
+                s = mass[:, :len(hist)].mean(axis=0) if hist else np.zeros(0)
+                np.testing.assert_allclose(r["scores"][h, :len(hist)], s, rtol=1e-12)
+                assert list(r["kept"][h]) == list(O.select_dynamic(s, m))
+            else:
+                want = [i for i, fid in enumerate(hist) if O.is_chunk_boundary(fid, Fc)]
+                while len(want) > Fh - Fc:
+                    want.pop(next(j for j, i in enumerate(want) if hist[i] != 0))
+                assert list(r["kept"][h]) == want
+            ids = r["ids"][h]
+            assert ids == [hist[f] for f in r["kept"][h]] + list(range(first, first + Fc))
+            assert len(ids) <= Fh
+            if ro.head_role[h] == O.DYNAMIC:
+                assert len(ids) == min(m, len(hist)) + Fc
+            lo, hi = int(r["tok_off"][h]), int(r["tok_off"][h + 1])
+            store = np.concatenate([ro.k[f * T:(f + 1) * T, h] for f in ids])
+            assert np.array_equal(r["k_c"][lo:hi], store)
+        prev_ids = r["ids"]
+        sizes.append(int(r["tok_off"][-1]))
+    # steady state: a static head reaches F_h - F_c kept frames and stays
+    assert sizes[-1] == sizes[-2] == sizes[-3]
+
+
+def test_rollout_rejects_budget_beyond_capacity():
+    w = W.small_workload(tokens_per_frame=4, num_heads=2, hist_frames=6, budget_m=4, seed=9)
+    ro = W.generate_rollout(w, 2)
+    with pytest.raises(ValueError):
+        O.rollout(ro.q, ro.k, ro.v, ro.head_role, 4, 4, 6, 3, w.query_stride)
