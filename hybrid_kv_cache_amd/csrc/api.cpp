@@ -71,7 +71,8 @@ fkv_status_t check_desc(const fkv_desc_t *d) {
 }
 
 struct Plan {
-  int H, D, T, Fh, Fc, Ft, s, n_q, n_win, n_s, m_eff, n_dyn;
+  int H, D, T, Fh, Fc, Ft, s, n_q, n_win, n_s, budget, n_dyn;
+  int fh[fkv::kMaxHeads];  // history frames of each head (F_h for a plain window)
   int dyn_index[fkv::kMaxHeads];
   int dyn_heads[fkv::kMaxHeads];
   uint64_t static_bits[fkv::kMaxHeads];
@@ -83,8 +84,10 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-fkv_status_t make_plan(const fkv_desc_t *d, const uint8_t *role, const uint8_t *mask,
-                       int32_t budget_m, Plan *p) {
+// hist_frames: per-head history lengths (a rolling cache), or null for a
+// plain window (every head has F_h).
+fkv_status_t make_plan(const fkv_desc_t *d, const int32_t *hist_frames, const uint8_t *role,
+                       const uint8_t *mask, int32_t budget_m, Plan *p) {
   fkv_status_t st = check_desc(d);
   if (st != FKV_OK) return st;
   if (!role) return fail(FKV_ERR_NULL, "head_role is NULL");
@@ -99,16 +102,20 @@ fkv_status_t make_plan(const fkv_desc_t *d, const uint8_t *role, const uint8_t *
   p->n_q = p->Fc * p->T;
   p->n_win = p->Ft * p->T;
   p->n_s = (p->n_q + p->s - 1) / p->s;
-  p->m_eff = budget_m < p->Fh ? budget_m : p->Fh;
+  p->budget = budget_m;
   p->n_dyn = 0;
   bool any_static = false;
   for (int h = 0; h < p->H; ++h) {
     if (role[h] != FKV_STATIC && role[h] != FKV_DYNAMIC)
       return fail(FKV_ERR_SHAPE, "head_role[%d] = %d is neither static (0) nor dynamic (1)", h,
                   role[h]);
-    any_static |= role[h] == FKV_STATIC;
+    const int fh = hist_frames ? hist_frames[h] : p->Fh;
+    if (fh < 0 || fh > p->Fh)
+      return fail(FKV_ERR_SHAPE, "hist_frames[%d] = %d outside [0, %d]", h, fh, p->Fh);
+    p->fh[h] = fh;
+    any_static |= role[h] == FKV_STATIC && fh > 0;
   }
-  if (any_static && p->Fh > 0 && !mask)
+  if (any_static && !mask)
     return fail(FKV_ERR_NULL, "static_keep_mask is NULL but static heads exist");
   p->seg_off[0] = 0;
   p->slot_off[0] = 0;
@@ -116,15 +123,24 @@ fkv_status_t make_plan(const fkv_desc_t *d, const uint8_t *role, const uint8_t *
   for (int h = 0; h < p->H; ++h) {
     int kept;
     p->static_bits[h] = 0;
+    p->dyn_index[h] = -1;
     if (role[h] == FKV_DYNAMIC) {
-      p->dyn_index[h] = p->n_dyn;
-      p->dyn_heads[p->n_dyn++] = h;
-      kept = p->m_eff;
+      // A dynamic head without history has nothing to score or keep.
+      if (p->fh[h] > 0) {
+        p->dyn_index[h] = p->n_dyn;
+        p->dyn_heads[p->n_dyn++] = h;
+      }
+      kept = budget_m < p->fh[h] ? budget_m : p->fh[h];
     } else {
-      p->dyn_index[h] = -1;
       uint64_t bits = 0;
-      for (int f = 0; f < p->Fh; ++f)
-        if (mask[(size_t)h * p->Fh + f]) bits |= 1ull << f;
+      for (int f = 0; f < p->Fh; ++f) {
+        if (!mask || !mask[(size_t)h * p->Fh + f]) continue;
+        if (f >= p->fh[h])
+          return fail(FKV_ERR_SHAPE,
+                      "static_keep_mask[%d][%d] marks a frame beyond the head's %d history "
+                      "frames", h, f, p->fh[h]);
+        bits |= 1ull << f;
+      }
       p->static_bits[h] = bits;
       kept = __builtin_popcountll(bits);
     }
@@ -136,18 +152,32 @@ fkv_status_t make_plan(const fkv_desc_t *d, const uint8_t *role, const uint8_t *
   for (int h = p->H; h < fkv::kMaxHeads; ++h) {
     p->dyn_index[h] = -1;
     p->static_bits[h] = 0;
+    p->fh[h] = 0;
   }
   for (int h = p->H + 1; h <= fkv::kMaxHeads; ++h) {
     p->seg_off[h] = p->seg_off[p->H];
     p->slot_off[h] = p->slot_off[p->H];
     p->tok_off[h] = p->tok_off[p->H];
   }
-  const bool score = p->n_dyn > 0 && p->Fh > 0;
-  const size_t lse_bytes = score ? (size_t)p->n_dyn * p->n_s * p->Ft * sizeof(float) : 0;
+  const size_t lse_bytes = p->n_dyn > 0 ? (size_t)p->n_dyn * p->n_s * p->Ft * sizeof(float) : 0;
   p->ws_lse_off = 0;
   p->ws_slot_off = align256(lse_bytes);
   p->ws_bytes = p->ws_slot_off + align256((size_t)p->slot_off[p->H] * sizeof(fkv::CopySlot));
   return FKV_OK;
+}
+
+fkv::WinView plain_window(const fkv_desc_t *d, const void *k, const void *v) {
+  const int eb = elt_bytes(d->dtype);
+  fkv::WinView w;
+  w.hist_k = reinterpret_cast<const char *>(k);
+  w.hist_v = reinterpret_cast<const char *>(v);
+  w.hist_off = nullptr;
+  w.tm_row_bytes = (int64_t)d->num_heads * d->head_dim * eb;
+  w.row_bytes = d->head_dim * eb;
+  const int64_t cur = (int64_t)d->hist_frames * d->tokens_per_frame * w.tm_row_bytes;
+  w.cur_k = w.hist_k + cur;
+  w.cur_v = w.hist_v + cur;
+  return w;
 }
 
 fkv_status_t hip_fail(hipError_t e, const char *what) {
@@ -185,29 +215,12 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-fkv_status_t fkv_plan(const fkv_desc_t *desc, const uint8_t *head_role,
-                      const uint8_t *static_keep_mask, int32_t budget_m, int64_t *kept_tokens,
-                      size_t *workspace_bytes) {
-  Plan p;
-  fkv_status_t st = make_plan(desc, head_role, static_keep_mask, budget_m, &p);
-  if (st != FKV_OK) return st;
-  if (kept_tokens) *kept_tokens = p.tok_off[p.H];
-  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
-  return ok();
-}
-
-fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_cache,
-                          const void *v_cache, const uint8_t *head_role,
-                          const uint8_t *static_keep_mask, int32_t budget_m, const fkv_ckv_t *out,
-                          void *workspace, size_t workspace_bytes, void *stream) {
-  Plan p;
-  fkv_status_t st = make_plan(desc, head_role, static_keep_mask, budget_m, &p);
-  if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+// Scoring, selection and compaction of one layer over the window `win`
+// (plain or rolling) with the plan p.
+fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
+                             const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  if (!q) return fail(FKV_ERR_NULL, "q is NULL");
   if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
   if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
     return fail(FKV_ERR_NULL, "a compressed-cache buffer (k, v, tok_off, seg_idx, seg_off) is NULL");
@@ -225,20 +238,22 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   const float c = log2e_scale(*desc);
 
   // 1. dynamic-head scoring: per (sampled query, frame) log-sum-exp
-  if (p.n_dyn > 0 && p.Fh > 0) {
+  if (p.n_dyn > 0) {
     fkv::ScoreArgs sa;
     sa.q = q;
-    sa.k = k_cache;
+    sa.win = win;
     sa.lse = lse;
     sa.H = p.H;
     sa.D = p.D;
     sa.T = p.T;
+    sa.F_c = p.Fc;
     sa.F_tot = p.Ft;
     sa.n_s = p.n_s;
     sa.stride = p.s;
     sa.n_dyn = p.n_dyn;
     sa.c = c;
     std::memcpy(sa.dyn_heads, p.dyn_heads, sizeof(sa.dyn_heads));
+    std::memcpy(sa.fh, p.fh, sizeof(sa.fh));
     hipError_t e = desc->dtype == FKV_BF16 ? fkv::launch_score_bf16(sa, s)
                                            : fkv::launch_score_f32(sa, s);
     if (e != hipSuccess) return hip_fail(e, "scoring kernel launch");
@@ -246,7 +261,7 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   // 2. selection, offsets and compaction slots
   {
     fkv::SelectArgs sa;
-    sa.lse = (p.n_dyn > 0 && p.Fh > 0) ? lse : nullptr;
+    sa.lse = p.n_dyn > 0 ? lse : nullptr;
     sa.seg_idx = out->seg_idx;
     sa.seg_off = out->seg_off;
     sa.tok_off = out->tok_off;
@@ -258,13 +273,10 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
     sa.F_c = p.Fc;
     sa.F_tot = p.Ft;
     sa.n_s = p.n_s;
-    sa.m_eff = p.m_eff;
-    for (int h = 0; h < fkv::kMaxHeads; ++h) {
-      // Without history there is nothing to score: every head is handled as
-      // static with an empty mask.
-      sa.dyn_index[h] = p.Fh > 0 ? p.dyn_index[h] : -1;
-      sa.static_bits[h] = p.static_bits[h];
-    }
+    sa.budget = p.budget;
+    std::memcpy(sa.fh, p.fh, sizeof(sa.fh));
+    std::memcpy(sa.dyn_index, p.dyn_index, sizeof(sa.dyn_index));
+    std::memcpy(sa.static_bits, p.static_bits, sizeof(sa.static_bits));
     std::memcpy(sa.seg_off_h, p.seg_off, sizeof(sa.seg_off_h));
     std::memcpy(sa.slot_off_h, p.slot_off, sizeof(sa.slot_off_h));
     std::memcpy(sa.tok_off_h, p.tok_off, sizeof(sa.tok_off_h));
@@ -274,19 +286,135 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   // 3. compaction
   {
     fkv::CompactArgs ca;
-    const int eb = elt_bytes(desc->dtype);
     ca.slots = slots;
-    ca.k = reinterpret_cast<const char *>(k_cache);
-    ca.v = reinterpret_cast<const char *>(v_cache);
+    ca.win = win;
     ca.k_out = reinterpret_cast<char *>(out->k);
     ca.v_out = reinterpret_cast<char *>(out->v);
-    ca.src_row_bytes = (int64_t)p.H * p.D * eb;
-    ca.row_bytes = p.D * eb;
-    ca.head_bytes = p.D * eb;
+    ca.out_tok_off = nullptr;
     ca.T = p.T;
+    ca.F_c = p.Fc;
     ca.chunks = (p.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
+    std::memcpy(ca.fh, p.fh, sizeof(ca.fh));
     hipError_t e = fkv::launch_compact(ca, p.slot_off[p.H], s);
     if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fkv_status_t fkv_plan(const fkv_desc_t *desc, const uint8_t *head_role,
+                      const uint8_t *static_keep_mask, int32_t budget_m, int64_t *kept_tokens,
+                      size_t *workspace_bytes) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (kept_tokens) *kept_tokens = p.tok_off[p.H];
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                          const void *v_cache, const uint8_t *head_role,
+                          const uint8_t *static_keep_mask, int32_t budget_m, const fkv_ckv_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
+                         workspace_bytes, stream);
+}
+
+fkv_status_t fkv_plan_ragged(const fkv_desc_t *desc, const int32_t *hist_frames,
+                             const uint8_t *head_role, const uint8_t *static_keep_mask,
+                             int32_t budget_m, int64_t *kept_tokens, size_t *workspace_bytes) {
+  if (!hist_frames) return fail(FKV_ERR_NULL, "hist_frames is NULL");
+  Plan p;
+  fkv_status_t st = make_plan(desc, hist_frames, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (kept_tokens) *kept_tokens = p.tok_off[p.H];
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+fkv_status_t fkv_compress_ragged(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *hist,
+                                 const int32_t *hist_frames, const void *cur_k,
+                                 const void *cur_v, const uint8_t *head_role,
+                                 const uint8_t *static_keep_mask, int32_t budget_m,
+                                 const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  if (!hist_frames) return fail(FKV_ERR_NULL, "hist_frames is NULL");
+  Plan p;
+  fkv_status_t st = make_plan(desc, hist_frames, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!hist || !hist->k || !hist->v || !hist->tok_off)
+    return fail(FKV_ERR_NULL, "history cache (k, v, tok_off) is NULL");
+  if (!cur_k || !cur_v) return fail(FKV_ERR_NULL, "cur_k or cur_v is NULL");
+  if (out && (out->k == hist->k || out->v == hist->v || out->tok_off == hist->tok_off))
+    return fail(FKV_ERR_SHAPE, "out must not share buffers with the history cache");
+  fkv::WinView win = plain_window(desc, hist->k, hist->v);
+  win.hist_off = hist->tok_off;
+  win.cur_k = reinterpret_cast<const char *>(cur_k);
+  win.cur_v = reinterpret_cast<const char *>(cur_v);
+  return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream);
+}
+
+fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, const void *cur_v,
+                                 const fkv_ckv_t *ckv, void *stream) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!cur_k || !cur_v) return fail(FKV_ERR_NULL, "cur_k or cur_v is NULL");
+  if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
+    return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  fkv::CompactArgs ca;
+  ca.slots = nullptr;
+  ca.win = plain_window(desc, nullptr, nullptr);
+  ca.win.cur_k = reinterpret_cast<const char *>(cur_k);
+  ca.win.cur_v = reinterpret_cast<const char *>(cur_v);
+  ca.k_out = reinterpret_cast<char *>(ckv->k);
+  ca.v_out = reinterpret_cast<char *>(ckv->v);
+  ca.out_tok_off = ckv->tok_off;
+  ca.T = desc->tokens_per_frame;
+  ca.F_c = desc->cur_frames;
+  ca.chunks = (ca.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
+  std::memset(ca.fh, 0, sizeof(ca.fh));  // every source frame is a current-chunk frame
+  hipError_t e = fkv::launch_compact(ca, desc->num_heads * desc->cur_frames,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
+  return ok();
+}
+
+fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
+                                  int32_t cur_frames, int32_t cap, uint8_t *mask) {
+  if (n_frames < 0 || n_frames > fkv::kMaxHistFrames)
+    return fail(FKV_ERR_SHAPE, "n_frames %d outside [0, %d]", n_frames, fkv::kMaxHistFrames);
+  if (cur_frames < 1) return fail(FKV_ERR_SHAPE, "cur_frames %d < 1", cur_frames);
+  if (cap < 0) return fail(FKV_ERR_SHAPE, "cap %d < 0", cap);
+  if (n_frames > 0 && (!frame_ids || !mask)) return fail(FKV_ERR_NULL, "frame_ids or mask is NULL");
+  int kept = 0;
+  for (int i = 0; i < n_frames; ++i) {
+    const int32_t id = frame_ids[i];
+    if (id < 0) return fail(FKV_ERR_SHAPE, "frame_ids[%d] = %d < 0", i, id);
+    const int32_t pos = id % cur_frames;
+    mask[i] = (id == 0 || pos == 0 || pos == cur_frames - 1) ? 1 : 0;
+    kept += mask[i];
+  }
+  // Over the cap: drop the oldest kept frames that are not the sink.
+  for (int i = 0; i < n_frames && kept > cap; ++i) {
+    if (mask[i] && frame_ids[i] != 0) {
+      mask[i] = 0;
+      --kept;
+    }
+  }
+  // Only sinks left above the cap: drop the oldest of them too.
+  for (int i = 0; i < n_frames && kept > cap; ++i) {
+    if (mask[i]) {
+      mask[i] = 0;
+      --kept;
+    }
   }
   return ok();
 }

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fkv_launch.h"
+
 namespace fkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -187,6 +189,24 @@ __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
+}
+
+// First byte of the T-row frame f of head h's window (fh_h history frames,
+// then the current chunk; see WinView), and the bytes between its rows.
+__device__ __forceinline__ const char *frame_rows(const WinView &w, bool want_v, int h, int fh_h,
+                                                  int f, int T, int64_t *row_stride) {
+  if (f < fh_h) {
+    const char *base = want_v ? w.hist_v : w.hist_k;
+    if (w.hist_off) {
+      *row_stride = w.row_bytes;
+      return base + (w.hist_off[h] + (int64_t)f * T) * w.row_bytes;
+    }
+    *row_stride = w.tm_row_bytes;
+    return base + (int64_t)f * T * w.tm_row_bytes + (int64_t)h * w.row_bytes;
+  }
+  const char *base = want_v ? w.cur_v : w.cur_k;
+  *row_stride = w.tm_row_bytes;
+  return base + (int64_t)(f - fh_h) * T * w.tm_row_bytes + (int64_t)h * w.row_bytes;
 }
 
 }  // namespace fkv

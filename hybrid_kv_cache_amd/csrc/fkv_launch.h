@@ -12,6 +12,23 @@ constexpr int kMaxHeads = 64;
 constexpr int kMaxHistFrames = 64;
 constexpr int kMaxCurFrames = 8;
 
+// Where the frames of each head's window live.  Frame f of head h is a
+// history frame when f < fh[h] (fh: the head's history length, in the
+// argument block that carries the view), else current-chunk frame f - fh[h].
+//  - History, token-major window (hist_off null): row r of head h at
+//    hist + r * tm_row_bytes + h * row_bytes.
+//  - History, ragged per head (a previous compressed cache): row r of head h
+//    at hist + (hist_off[h] + r) * row_bytes.
+//  - Current chunk, token-major [F_c T, H, D]: row r of head h at
+//    cur + r * tm_row_bytes + h * row_bytes.
+struct WinView {
+  const char *hist_k, *hist_v;
+  const int64_t *hist_off;   // [H + 1] device row offsets, or null
+  const char *cur_k, *cur_v;
+  int64_t tm_row_bytes;      // H * D * elt
+  int32_t row_bytes;         // D * elt
+};
+
 // One copy job of the compaction: the T rows of window frame src_frame of
 // head `head` go to compacted rows dst_row .. dst_row + T - 1.
 struct CopySlot {
@@ -22,14 +39,15 @@ struct CopySlot {
 
 // Per-(dynamic head, sampled query, window frame) log-sum-exp of the scaled
 // logits in base 2: lse[(d * n_s + r) * F_tot + f] = log2 sum_{j in f} 2^(c q.k_j),
-// with c = scale * log2(e).
+// with c = scale * log2(e), for f < fh[h] + F_c (F_tot: the largest window).
 struct ScoreArgs {
   const void *q;        // [Nq, H, D]
-  const void *k;        // [N_win, H, D]
+  WinView win;
   float *lse;           // [n_dyn, n_s, F_tot]
-  int32_t H, D, T, F_tot, n_s, stride, n_dyn;
+  int32_t H, D, T, F_c, F_tot, n_s, stride, n_dyn;
   float c;
   int32_t dyn_heads[kMaxHeads];
+  int32_t fh[kMaxHeads];
 };
 
 struct SelectArgs {
@@ -39,7 +57,8 @@ struct SelectArgs {
   int64_t *tok_off;     // [H + 1]
   float *seg_score;     // [H * F_h] or null
   CopySlot *slots;      // [total_slots]
-  int32_t H, T, F_h, F_c, F_tot, n_s, m_eff;
+  int32_t H, T, F_h, F_c, F_tot, n_s, budget;  // F_h: row length of seg_score
+  int32_t fh[kMaxHeads];            // history frames of each head
   int32_t dyn_index[kMaxHeads];     // -1 static, else row block in lse
   uint64_t static_bits[kMaxHeads];  // kept history frames of static heads
   int32_t seg_off_h[kMaxHeads + 1];
@@ -47,17 +66,19 @@ struct SelectArgs {
   int64_t tok_off_h[kMaxHeads + 1];
 };
 
+// Compaction.  With slots: one job per slot (head, window frame, rows).
+// Without (slots null): the current chunk only, slot s = (head s / F_c,
+// current frame s % F_c) going to the last F_c frames of the head's range in
+// out_tok_off (the selection of an earlier call reused).
 struct CompactArgs {
   const CopySlot *slots;
-  const char *k;        // [N_win, H, D] bytes
-  const char *v;
+  WinView win;
   char *k_out;          // [rows, D]
   char *v_out;
-  int64_t src_row_bytes;  // H * D * elt
-  int32_t row_bytes;      // D * elt
-  int32_t head_bytes;     // D * elt (offset of head h inside a token row = h * head_bytes)
-  int32_t T;
+  const int64_t *out_tok_off;  // [H + 1], read when slots is null
+  int32_t T, F_c;
   int32_t chunks;         // ceil(T / kCompactRows)
+  int32_t fh[kMaxHeads];
 };
 constexpr int kCompactRows = 64;
 

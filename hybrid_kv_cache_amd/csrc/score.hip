@@ -51,10 +51,11 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   // index; readfirstlane tells the compiler it is wave-uniform, so the K
   // buffer resource stays in scalar registers.
   const int h = __builtin_amdgcn_readfirstlane(a.dyn_heads[di]);
+  const int fh_h = __builtin_amdgcn_readfirstlane(a.fh[h]);
   const int f = blockIdx.y;
+  if (f >= fh_h + a.F_c) return;  // beyond this head's window
   const int r = blockIdx.x * kBM + wave * 32 + col;   // sampled row
   const int64_t hd = (int64_t)a.H * kD;
-  const int64_t rs_bytes = hd * 2;
 
   bf16x8 qf[8];
   if (r < a.n_s) {
@@ -67,9 +68,9 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
     for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
   }
 
-  // K rows of frame f, head h: row j at kbase + j * H * D elements.
-  const char *kframe = reinterpret_cast<const char *>(a.k) +
-                       ((int64_t)f * a.T * hd + (int64_t)h * kD) * 2;
+  // K rows of frame f of head h's window, rs_bytes apart.
+  int64_t rs_bytes;
+  const char *kframe = frame_rows(a.win, false, h, fh_h, f, a.T, &rs_bytes);
   const int len = a.T;
   const int ntiles = (len + kKT - 1) / kKT;
   const int lrow = lane >> 4, lpos = lane & 15;
@@ -186,11 +187,13 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
   const float *qp = reinterpret_cast<const float *>(a.q) + (int64_t)r * a.stride * hd + (int64_t)h * D;
   for (int d = tid; d < D; d += 256) qs[d] = qp[d];
   __syncthreads();
-  const float *kbase = reinterpret_cast<const float *>(a.k) + (int64_t)h * D;
-  for (int f = 0; f < a.F_tot; ++f) {
+  const int fh_h = a.fh[h];
+  for (int f = 0; f < fh_h + a.F_c; ++f) {
+    int64_t rs_bytes;
+    const char *kframe = frame_rows(a.win, false, h, fh_h, f, a.T, &rs_bytes);
     float m = kNegBig, l = 0.f;
     for (int j = tid; j < a.T; j += 256) {
-      const float *kp = kbase + ((int64_t)f * a.T + j) * hd;
+      const float *kp = reinterpret_cast<const float *>(kframe + j * rs_bytes);
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qs[d], kp[d], s);

@@ -6,9 +6,11 @@
 //   3 (dynamic similarity pruning): a dynamic head keeps the few frames with
 //     the highest attention scores against the current queries.
 // Score of history frame f of a dynamic head = mean over the sampled queries
-// of the softmax mass of frame f (softmax over the whole window); the kept
-// set is the min(m, F_h) best frames, ties broken by the lower frame index,
-// emitted in ascending frame order.
+// of the softmax mass of frame f (softmax over the head's whole window); the
+// kept set is the min(m, fh) best of the head's fh history frames, ties
+// broken by the lower frame index, emitted in ascending frame order.  (fh is
+// F_h for every head of a plain window; a rolling cache gives each head its
+// own history length.)
 //
 // One workgroup (4 waves) per head.  Dynamic heads: one sampled query per
 // thread at a time, the softmax over its frames in registers, masses summed
@@ -42,12 +44,13 @@ __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib)
 constexpr int kSelWaves = 4;
 
 // Masses of one dynamic head: thread t takes sampled queries t, t + 256, ...;
-// for each, the F_tot frame log-sum-exps (base 2) become a softmax over
-// frames, whose first F_h entries are added to per-thread sums.  The sums
-// are reduced over each wave with shuffles and stored per wave in part[w][f].
+// for each, the ft frame log-sum-exps (base 2; rows F_tot apart) become a
+// softmax over the head's window, whose first fh entries (the history) are
+// added to per-thread sums.  The sums are reduced over each wave with
+// shuffles and stored per wave in part[w][f].
 template <int FT>
-__device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int F_h,
-                                                  float (*part)[64], int tid, int lane,
+__device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int ft,
+                                                  int fh, float (*part)[64], int tid, int lane,
                                                   int wave) {
   float acc[FT];
 #pragma unroll
@@ -56,7 +59,7 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
     const float *row = base + (int64_t)r * F_tot;
     float v[FT];
 #pragma unroll
-    for (int f = 0; f < FT; ++f) v[f] = f < F_tot ? row[f] : -INFINITY;
+    for (int f = 0; f < FT; ++f) v[f] = f < ft ? row[f] : -INFINITY;
     float M = v[0];
 #pragma unroll
     for (int f = 1; f < FT; ++f) M = fmaxf(M, v[f]);
@@ -72,7 +75,7 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
   }
 #pragma unroll
   for (int f = 0; f < FT && f < 64; ++f) {
-    if (f < F_h) {
+    if (f < fh) {
       const float x = wave_sum(acc[f]);
       if (lane == 0) part[wave][f] = x;
     }
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
   const int di = a.dyn_index[h];
+  const int fh = a.fh[h];  // this head's history frames
 
   if (tid == 0) {
     a.seg_off[h] = a.seg_off_h[h];
@@ -103,23 +107,26 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
     // over frames, masses accumulated per thread; then a fixed-order
     // reduction over threads (deterministic).
     const float *base = a.lse + (int64_t)di * a.n_s * a.F_tot;
-    if (a.F_tot <= 24)
-      accumulate_masses<24>(base, a.n_s, a.F_tot, a.F_h, part, tid, lane, wave);
+    const int ft = fh + a.F_c;
+    if (ft <= 24)
+      accumulate_masses<24>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
     else
-      accumulate_masses<72>(base, a.n_s, a.F_tot, a.F_h, part, tid, lane, wave);
+      accumulate_masses<72>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
     __syncthreads();
     if (wave == 0) {
       float score = -INFINITY;
-      if (lane < a.F_h) {
+      if (lane < fh) {
         float sum = part[0][lane];
 #pragma unroll
         for (int w = 1; w < kSelWaves; ++w) sum += part[w][lane];
         score = sum / (float)a.n_s;
         if (a.seg_score) a.seg_score[(int64_t)h * a.F_h + lane] = score;
+      } else if (a.seg_score && lane < a.F_h) {
+        a.seg_score[(int64_t)h * a.F_h + lane] = __builtin_nanf("");
       }
       // Bitonic sort of 64 (score, frame) pairs into ranking order.  A NaN
       // score ranks like -inf, so the m_eff first entries are always real
-      // frames (lanes >= F_h carry -inf and larger indices).
+      // frames (lanes >= fh carry -inf and larger indices).
       float s = score != score ? -INFINITY : score;
       int idx = lane;
 #pragma unroll
@@ -141,7 +148,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
         }
       }
       // Lane i now holds the i-th ranked frame; OR together the first m_eff.
-      unsigned long long bits = lane < a.m_eff ? (1ull << idx) : 0ull;
+      const int m_eff = min(a.budget, fh);
+      unsigned long long bits = lane < m_eff ? (1ull << idx) : 0ull;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) bits |= __shfl_xor(bits, off, 64);
       if (lane == 0) kept_bits_s = bits;
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
   }
   __syncthreads();
   const unsigned long long bits = kept_bits_s;
-  if (tid < a.F_h && ((bits >> tid) & 1ull)) {
+  if (tid < fh && ((bits >> tid) & 1ull)) {
     const int pos = __popcll(bits & ((1ull << tid) - 1ull));
     a.seg_idx[a.seg_off_h[h] + pos] = tid;
   }
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
       for (int i = 0; i < tid; ++i) b &= b - 1ull;
       src = __ffsll((long long)b) - 1;
     } else {
-      src = a.F_h + (tid - kept);
+      src = fh + (tid - kept);
     }
     CopySlot sl;
     sl.head = h;

@@ -24,8 +24,9 @@ FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
 FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
-EXPORTED = ("fkv_plan", "fkv_compress", "fkv_attend_workspace", "fkv_attend",
-            "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
+            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_attend_workspace",
+            "fkv_attend", "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
 
 
 class FkvDesc(ctypes.Structure):
@@ -64,11 +65,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(SZ)]
     lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                  ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_plan_ragged.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, I32, ctypes.POINTER(I64),
+                                    ctypes.POINTER(SZ)]
+    lib.fkv_compress_ragged.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P,
+                                        P, P, P, P, I32, ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_refresh_current.argtypes = [ctypes.POINTER(FkvDesc), P, P, ctypes.POINTER(FkvCkv), P]
+    lib.fkv_roll_static_mask.argtypes = [I32, P, I32, I32, P]
     lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
-    for name in ("fkv_plan", "fkv_compress", "fkv_attend_workspace", "fkv_attend",
-                 "fkv_attend_dense"):
+    for name in ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
+                 "fkv_refresh_current", "fkv_roll_static_mask", "fkv_attend_workspace",
+                 "fkv_attend", "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fkv_status_str.argtypes = [ctypes.c_int]
     lib.fkv_status_str.restype = ctypes.c_char_p
@@ -124,14 +132,48 @@ def fkv_plan(desc: FkvDesc, head_role, static_keep_mask, budget_m: int):
     return kept.value, ws.value
 
 
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def fkv_plan_ragged(desc: FkvDesc, hist_frames, head_role, static_keep_mask, budget_m: int):
+    """Returns (kept_tokens, workspace_bytes) for per-head history lengths."""
+    lib = load()
+    fh = _host_i32(hist_frames)
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    kept = ctypes.c_int64(0)
+    ws = ctypes.c_size_t(0)
+    _check(lib.fkv_plan_ragged(ctypes.byref(desc), fh.ctypes.data, role.ctypes.data,
+                               mask.ctypes.data if mask.size else None, int(budget_m),
+                               ctypes.byref(kept), ctypes.byref(ws)))
+    return kept.value, ws.value
+
+
+def fkv_roll_static_mask(frame_ids, cur_frames: int, cap: int) -> np.ndarray:
+    """Keep mask (uint8) of a static head's history frames in a rolling cache."""
+    lib = load()
+    ids = _host_i32(frame_ids)
+    mask = np.zeros(len(ids), dtype=np.uint8)
+    _check(lib.fkv_roll_static_mask(len(ids), ids.ctypes.data if len(ids) else None,
+                                    int(cur_frames), int(cap),
+                                    mask.ctypes.data if len(ids) else None))
+    return mask
+
+
 class CompressedKV:
-    """Device buffers of one layer's compressed cache, allocated with torch."""
+    """Device buffers of one layer's compressed cache, allocated with torch.
+    With hist_frames (per-head history lengths), sized for fkv_compress_ragged."""
 
     def __init__(self, desc: FkvDesc, head_role, static_keep_mask, budget_m: int,
-                 device="cuda", with_scores: bool = True):
+                 device="cuda", with_scores: bool = True, hist_frames=None):
         import torch
-        self.kept_tokens, self.workspace_bytes = fkv_plan(desc, head_role, static_keep_mask,
-                                                          budget_m)
+        if hist_frames is None:
+            self.kept_tokens, self.workspace_bytes = fkv_plan(desc, head_role, static_keep_mask,
+                                                              budget_m)
+        else:
+            self.kept_tokens, self.workspace_bytes = fkv_plan_ragged(
+                desc, hist_frames, head_role, static_keep_mask, budget_m)
         H, D, Fh = desc.num_heads, desc.head_dim, desc.hist_frames
         dt = torch.bfloat16 if desc.dtype == FKV_BF16 else torch.float32
         self.k = torch.empty((max(self.kept_tokens, 1), D), dtype=dt, device=device)
@@ -161,6 +203,29 @@ def fkv_compress(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask
                             role.ctypes.data, mask.ctypes.data if mask.size else None,
                             int(budget_m), ctypes.byref(out), _ptr(ckv.workspace),
                             ckv.workspace_bytes, _stream(stream)))
+
+
+def fkv_compress_ragged(desc: FkvDesc, q, hist: CompressedKV, hist_frames, cur_k, cur_v,
+                        head_role, static_keep_mask, budget_m: int, ckv: CompressedKV,
+                        stream=None) -> None:
+    lib = load()
+    fh = _host_i32(hist_frames)
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    h = hist.struct()
+    out = ckv.struct()
+    _check(lib.fkv_compress_ragged(ctypes.byref(desc), _ptr(q), ctypes.byref(h), fh.ctypes.data,
+                                   _ptr(cur_k), _ptr(cur_v), role.ctypes.data,
+                                   mask.ctypes.data if mask.size else None, int(budget_m),
+                                   ctypes.byref(out), _ptr(ckv.workspace), ckv.workspace_bytes,
+                                   _stream(stream)))
+
+
+def fkv_refresh_current(desc: FkvDesc, cur_k, cur_v, ckv: CompressedKV, stream=None) -> None:
+    lib = load()
+    s = ckv.struct()
+    _check(lib.fkv_refresh_current(ctypes.byref(desc), _ptr(cur_k), _ptr(cur_v), ctypes.byref(s),
+                                   _stream(stream)))
 
 
 def fkv_attend_workspace(desc: FkvDesc) -> int:
@@ -226,3 +291,78 @@ def to_host(t) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+class RollingCache:
+    """One layer's compressed cache carried across chunk steps: the cache
+    written for chunk c (kept history + chunk c's frames) is chunk c + 1's
+    history.  Two device buffers of the largest possible size alternate.
+
+    Host bookkeeping only: each head's history length, and the absolute frame
+    ids of static heads' frames (needed for their keep rule, which
+    fkv_roll_static_mask applies); dynamic heads' kept ids live on the device
+    (seg_idx) and are recorded here as -1.
+    """
+
+    def __init__(self, desc: FkvDesc, head_role, budget_m: int, device="cuda"):
+        self.desc = desc
+        self.role = np.asarray(head_role, dtype=np.uint8)
+        self.m = int(budget_m)
+        H, Fh, Fc = desc.num_heads, desc.hist_frames, desc.cur_frames
+        if self.m > Fh - Fc:
+            raise ValueError("a rolling cache needs budget_m <= hist_frames - cur_frames")
+        full = np.ones((H, Fh), dtype=np.uint8)
+        self.bufs = [CompressedKV(desc, self.role, full, self.m, device=device,
+                                  hist_frames=[Fh] * H) for _ in range(2)]
+        self.which = 0
+        self.chunk = 0
+        self.ids = None          # per head: frame ids of the current cache's frames
+        self.rows = 0            # rows written by the last step
+        self.mask = None
+
+    @property
+    def cache(self) -> CompressedKV:
+        return self.bufs[self.which]
+
+    def _masks(self, hist_ids):
+        H, Fh, Fc = self.desc.num_heads, self.desc.hist_frames, self.desc.cur_frames
+        mask = np.zeros((H, Fh), dtype=np.uint8)
+        for h in range(H):
+            if self.role[h] == 0:
+                mk = fkv_roll_static_mask(hist_ids[h], Fc, Fh - Fc)
+                mask[h, :len(mk)] = mk
+        return mask
+
+    def step(self, q, cur_k, cur_v, window_k=None, window_v=None, stream=None):
+        """Compress chunk self.chunk.  The first chunk takes the plain window
+        (window_k / window_v [N_win, H, D], whose last F_c frames are cur_k /
+        cur_v); later chunks take only the current chunk [F_c T, H, D]."""
+        d = self.desc
+        H, Fh, Fc, T = d.num_heads, d.hist_frames, d.cur_frames, d.tokens_per_frame
+        first = Fh + self.chunk * Fc
+        if self.chunk == 0:
+            hist_ids = [list(range(Fh))] * H
+            self.mask = self._masks(hist_ids)
+            out = self.bufs[self.which]
+            fkv_compress(d, q, window_k, window_v, self.role, self.mask, self.m, out, stream)
+            self.rows, _ = fkv_plan(d, self.role, self.mask, self.m)
+        else:
+            hist_ids = self.ids
+            hist_frames = [len(x) for x in hist_ids]
+            self.mask = self._masks(hist_ids)
+            src = self.bufs[self.which]
+            self.which ^= 1
+            out = self.bufs[self.which]
+            fkv_compress_ragged(d, q, src, hist_frames, cur_k, cur_v, self.role, self.mask,
+                                self.m, out, stream)
+            self.rows, _ = fkv_plan_ragged(d, hist_frames, self.role, self.mask, self.m)
+        new_ids = []
+        for h in range(H):
+            if self.role[h] == 0:
+                kept = [hist_ids[h][f] for f in np.flatnonzero(self.mask[h, :len(hist_ids[h])])]
+            else:
+                kept = [-1] * min(self.m, len(hist_ids[h]))
+            new_ids.append(kept + list(range(first, first + Fc)))
+        self.ids = new_ids
+        self.chunk += 1
+        return self.cache

@@ -117,6 +117,56 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
                           const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* ---- Rolling compressed cache (a chunk's compressed cache is the next
+ * chunk's history) ----------------------------------------------------------
+ * [S] 输出与工程收益: the compressed K/V replace the layer's cache.  Kept here
+ * as the cache itself: after chunk c the compressed cache holds, per head, its
+ * kept history frames and chunk c's (now finished) frames; frames not kept are
+ * gone, and chunk c + 1 compresses that per-head history together with its own
+ * current chunk.  The history of head h is then hist_frames[h] frames (of T
+ * rows each) at rows [hist->tok_off[h], hist->tok_off[h+1]) of hist->k /
+ * hist->v, which must agree with hist_frames[h] * T; desc->hist_frames is the
+ * largest history any head may have (the row length of static_keep_mask). */
+
+/* As fkv_plan, for per-head history lengths hist_frames[H] (host array,
+ * 0 <= hist_frames[h] <= desc->hist_frames): a dynamic head keeps
+ * min(m, hist_frames[h]) frames, a static head the frames its mask row marks,
+ * which must all lie below hist_frames[h] (else FKV_ERR_SHAPE). */
+fkv_status_t fkv_plan_ragged(const fkv_desc_t *desc, const int32_t *hist_frames,
+                             const uint8_t *head_role, const uint8_t *static_keep_mask,
+                             int32_t budget_m, int64_t *kept_tokens, size_t *workspace_bytes);
+
+/* As fkv_compress, with each head's window = its history in `hist` (a
+ * compressed cache written by an earlier fkv_compress or
+ * fkv_compress_ragged; only k, v and tok_off are read) followed by the current
+ * chunk cur_k / cur_v [F_c T, H, D] (token-major, device).  Scoring uses the
+ * softmax over the head's whole window.  `out` receives the new compressed
+ * cache and must not share buffers with `hist`. */
+fkv_status_t fkv_compress_ragged(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *hist,
+                                 const int32_t *hist_frames, const void *cur_k,
+                                 const void *cur_v, const uint8_t *head_role,
+                                 const uint8_t *static_keep_mask, int32_t budget_m,
+                                 const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Selection reused across the denoising steps of one chunk: copies the
+ * current chunk cur_k / cur_v [F_c T, H, D] into the last F_c frames of every
+ * head's range of ckv (which an earlier compression of this layer and chunk
+ * wrote, offsets included); the kept history rows are left as they are. */
+fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, const void *cur_v,
+                                 const fkv_ckv_t *ckv, void *stream);
+
+/* Host helper: the keep mask of a static head's history in a rolling cache.
+ * frame_ids[n_frames] are the absolute ids (>= 0, counting frames from the
+ * start of the video; chunks are the aligned runs of cur_frames ids) of the
+ * head's history frames, oldest first.  Marks the sink (id 0) and the first
+ * and last frame of every chunk ([S] 关键模块 1 and 2: static heads attend to
+ * chunk start and end positions), then, while more than cap are marked,
+ * unmarks the oldest marked frame that is not a sink (sinks last).  With
+ * cap = desc->hist_frames - cur_frames no history outgrows the window. */
+fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
+                                  int32_t cur_frames, int32_t cap, uint8_t *mask);
+
 /* Bytes of the optional attention workspace for the current HIP device: the
  * bf16 attention can then split its work into equal parts, one per resident
  * workgroup (two per compute unit), whatever the number of (head, 128-query)

@@ -190,3 +190,102 @@ def test_attend_workspace_query(lib):
     assert n.value == 0
     d.head_dim = 96
     assert lib.fkv_attend_workspace(ctypes.byref(d), ctypes.byref(n)) == fkv.FKV_ERR_DTYPE
+
+
+# ---- rolling cache: host logic ---------------------------------------------
+
+def test_roll_static_mask_matches_oracle(lib):
+    """The library's keep rule for static heads in a rolling cache against the
+    oracle's, on random histories (sorted distinct ids, with and without the
+    sink) and caps."""
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        fc = int(rng.integers(1, 6))
+        n = int(rng.integers(0, 40))
+        ids = sorted(rng.choice(200, n, replace=False).tolist())
+        if n and rng.random() < 0.5:
+            ids[0] = 0
+            ids = sorted(set(ids))
+        cap = int(rng.integers(0, 20))
+        got = fkv.fkv_roll_static_mask(ids, fc, cap)
+        assert np.array_equal(got, O.roll_static_keep(ids, fc, cap)), (ids, fc, cap)
+
+
+def test_roll_static_mask_errors(lib):
+    m = (ctypes.c_uint8 * 4)()
+    ids = (ctypes.c_int32 * 4)(0, 1, -2, 3)
+    assert lib.fkv_roll_static_mask(4, ids, 3, 2, m) == fkv.FKV_ERR_SHAPE
+    assert lib.fkv_roll_static_mask(65, ids, 3, 2, m) == fkv.FKV_ERR_SHAPE
+    assert lib.fkv_roll_static_mask(4, None, 3, 2, m) == fkv.FKV_ERR_NULL
+    assert lib.fkv_roll_static_mask(4, ids, 0, 2, m) == fkv.FKV_ERR_SHAPE
+    assert lib.fkv_roll_static_mask(0, None, 3, 2, None) == fkv.FKV_OK
+
+
+def test_plan_ragged_matches_oracle_offsets(lib):
+    """Kept rows for per-head history lengths: the oracle's ragged compression
+    on random histories gives the same total."""
+    rng = np.random.default_rng(1)
+    for trial in range(60):
+        H, Fh, Fc, T = int(rng.integers(1, 7)), int(rng.integers(0, 12)), 3, 4
+        m = int(rng.integers(0, 6))
+        role = rng.integers(0, 2, H).astype(np.uint8)
+        fh = rng.integers(0, Fh + 1, H).astype(np.int32)
+        mask = np.zeros((H, max(Fh, 1)), dtype=np.uint8)[:, :Fh]
+        for h in range(H):
+            mask[h, :fh[h]] = rng.integers(0, 2, fh[h])
+        d = fkv.make_desc(H, 128, T, Fh, Fc, 2)
+        kept, ws = fkv.fkv_plan_ragged(d, fh, role, mask, m)
+        want = sum((min(m, fh[h]) if role[h] else int(mask[h].sum())) + Fc for h in range(H)) * T
+        assert kept == want, trial
+        # the oracle's ragged compaction writes the same number of rows
+        off = np.concatenate([[0], np.cumsum(fh.astype(np.int64) * T)])
+        D = 8
+        hk = np.zeros((int(off[-1]), D), dtype=np.float32)
+        cur = np.zeros((Fc * T, H, D), dtype=np.float32)
+        q = np.zeros((Fc * T, H, D), dtype=np.float32)
+        r = O.compress_ragged(q, hk, hk, off, cur, cur, role, mask, m, T, Fc, 2)
+        assert int(r["tok_off"][-1]) == kept
+
+
+def test_plan_ragged_errors(lib):
+    d = fkv.make_desc(2, 128, 8, 6, 3, 2)
+    role = np.array([0, 1], dtype=np.uint8)
+    mask = np.zeros((2, 6), dtype=np.uint8)
+    with pytest.raises(fkv.FkvError, match="hist_frames"):
+        fkv.fkv_plan_ragged(d, [7, 2], role, mask, 2)      # beyond desc.hist_frames
+    with pytest.raises(fkv.FkvError, match="hist_frames"):
+        fkv.fkv_plan_ragged(d, [-1, 2], role, mask, 2)
+    mask[0, 4] = 1
+    with pytest.raises(fkv.FkvError, match="beyond the head"):
+        fkv.fkv_plan_ragged(d, [3, 2], role, mask, 2)      # static mark past its history
+    assert fkv.fkv_plan_ragged(d, [5, 0], role, mask, 2)[0] == (1 + 3 + 0 + 3) * 8
+    kept = ctypes.c_int64(0)
+    assert lib.fkv_plan_ragged(ctypes.byref(d), None, role.ctypes.data, mask.ctypes.data, 2,
+                               ctypes.byref(kept), None) == fkv.FKV_ERR_NULL
+
+
+def test_compress_ragged_and_refresh_argument_errors(lib):
+    d = fkv.make_desc(2, 128, 8, 6, 3, 2)
+    role = np.array([0, 1], dtype=np.uint8)
+    mask = np.zeros((2, 6), dtype=np.uint8)
+    fh = np.array([4, 4], dtype=np.int32)
+    hist = fkv.FkvCkv(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None, 1000)
+    out = fkv.FkvCkv(0x1000, 0x6000, 0x7000, 0x8000, 0x9000, None, 1000)
+    # out sharing a buffer with the history
+    st = lib.fkv_compress_ragged(ctypes.byref(d), 0x100, ctypes.byref(hist), fh.ctypes.data,
+                                 0x200, 0x300, role.ctypes.data, mask.ctypes.data, 2,
+                                 ctypes.byref(out), 0x400, 1 << 20, None)
+    assert st == fkv.FKV_ERR_SHAPE
+    st = lib.fkv_compress_ragged(ctypes.byref(d), 0x100, ctypes.byref(hist), None, 0x200, 0x300,
+                                 role.ctypes.data, mask.ctypes.data, 2, ctypes.byref(out),
+                                 0x400, 1 << 20, None)
+    assert st == fkv.FKV_ERR_NULL
+    st = lib.fkv_compress_ragged(ctypes.byref(d), 0x100, ctypes.byref(hist), fh.ctypes.data,
+                                 None, 0x300, role.ctypes.data, mask.ctypes.data, 2,
+                                 ctypes.byref(out), 0x400, 1 << 20, None)
+    assert st == fkv.FKV_ERR_NULL
+    ck = fkv.FkvCkv(None, None, None, None, None, None, 0)
+    assert lib.fkv_refresh_current(ctypes.byref(d), 0x100, 0x200, ctypes.byref(ck),
+                                   None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_refresh_current(ctypes.byref(d), None, 0x200, ctypes.byref(hist),
+                                   None) == fkv.FKV_ERR_NULL

@@ -1,0 +1,194 @@
+"""GPU parity of the rolling compressed cache (fkv_compress_ragged,
+fkv_refresh_current, the RollingCache bookkeeping) against the CPU oracle."""
+import numpy as np
+import pytest
+
+from hybrid_kv_cache_amd import fkv
+from hybrid_kv_cache_amd import workloads as W
+from oracle import forcing_kv as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.require_gpu()
+
+
+class _Hist:
+    """A history cache held in device tensors (k, v, tok_off)."""
+
+    def __init__(self, k, v, tok_off):
+        self.k, self.v = fkv.to_device(k), fkv.to_device(v)
+        self.tok_off = fkv.to_device(np.asarray(tok_off, dtype=np.int64))
+        self.rows = int(tok_off[-1])
+
+    def struct(self):
+        return fkv.FkvCkv(self.k.data_ptr(), self.v.data_ptr(), self.tok_off.data_ptr(), None,
+                          None, None, self.rows)
+
+
+def _host_results(ckv, H, Fh):
+    return dict(seg_off=fkv.to_host(ckv.seg_off), tok_off=fkv.to_host(ckv.tok_off),
+                seg_idx=fkv.to_host(ckv.seg_idx)[:H * Fh],
+                seg_score=fkv.to_host(ckv.seg_score)[:H * Fh].reshape(H, Fh))
+
+
+def _check_ragged(w, res, ref, role, mask, m):
+    """Scores to 1e-3, kept frames exact outside the cutoff tie band, offsets
+    exact; returns the GPU kept frames per head."""
+    H, T, Fc = w.num_heads, w.tokens_per_frame, w.cur_frames
+    G.check_scores(res, ref["scores"], role)
+    kept = [np.array(res["seg_idx"][res["seg_off"][h]:res["seg_off"][h + 1]]) for h in range(H)]
+    for h in range(H):
+        n_h = int(ref["n_hist"][h])
+        g = list(kept[h])
+        assert g == sorted(set(g)) and all(0 <= f < n_h for f in g), (h, g)
+        if role[h] == O.DYNAMIC:
+            assert O.kept_set_valid(g, ref["scores"][h, :n_h], m), (h, g, ref["scores"][h])
+        else:
+            assert g == list(np.flatnonzero(mask[h, :n_h])), (h, g)
+    _, seg_off, tok_off = O.offsets(kept, T, Fc)
+    np.testing.assert_array_equal(res["seg_off"], seg_off)
+    np.testing.assert_array_equal(res["tok_off"], tok_off)
+    return kept
+
+
+@pytest.mark.parametrize("dtype,T,seed", [("bf16", 100, 1), ("bf16", 37, 2), ("f32", 40, 3)])
+def test_compress_ragged_random_histories(dtype, T, seed):
+    """Per-head histories of random lengths (0 .. F_h frames, drawn from a frame
+    store in random order), a current chunk, mixed roles: scores, kept frames,
+    offsets and compacted rows against the oracle, then attention over the new
+    cache."""
+    import torch
+    D = 128 if dtype == "bf16" else 64
+    w = W.small_workload(name=f"ragged_{dtype}", dtype=dtype, head_dim=D, tokens_per_frame=T,
+                         num_heads=5, hist_frames=9, budget_m=3, num_static=2, query_stride=3,
+                         seed=seed)
+    ro = W.generate_rollout(w, 4, seed=100 + seed)
+    H, Fh, Fc = w.num_heads, w.hist_frames, w.cur_frames
+    rng = np.random.default_rng(seed)
+    n_hist = rng.integers(0, Fh + 1, H)
+    n_hist[0] = 0          # a head without history
+    n_hist[-1] = Fh        # a full one
+    store_frames = (Fh + 4 * Fc)
+    hk, hv, off = [], [], [0]
+    for h in range(H):
+        fr = rng.choice(store_frames - Fc, n_hist[h], replace=False)
+        for f in fr:
+            hk.append(ro.k[f * T:(f + 1) * T, h])
+            hv.append(ro.v[f * T:(f + 1) * T, h])
+        off.append(off[-1] + n_hist[h] * T)
+    shape = (0, D)
+    hk = np.concatenate(hk) if hk else np.zeros(shape, ro.k.dtype)
+    hv = np.concatenate(hv) if hv else np.zeros(shape, ro.v.dtype)
+    role = ro.head_role
+    mask = np.zeros((H, Fh), dtype=np.uint8)
+    for h in range(H):
+        mask[h, :n_hist[h]] = rng.integers(0, 2, n_hist[h])
+    cur_k, cur_v, q = ro.current("k", 3), ro.current("v", 3), ro.q[3]
+    ref = O.compress_ragged(q, hk, hv, np.array(off), cur_k, cur_v, role, mask, w.budget_m, T,
+                            Fc, w.query_stride)
+
+    desc = fkv.desc_for(w)
+    hist = _Hist(hk if len(hk) else np.zeros((1, D), ro.k.dtype),
+                 hv if len(hv) else np.zeros((1, D), ro.v.dtype), off)
+    ckv = fkv.CompressedKV(desc, role, mask, w.budget_m, hist_frames=n_hist)
+    qd, ckd, cvd = fkv.to_device(q), fkv.to_device(cur_k), fkv.to_device(cur_v)
+    G.announce(f"fkv_compress_ragged {dtype} T={T} hist={list(n_hist)}")
+    fkv.fkv_compress_ragged(desc, qd, hist, n_hist, ckd, cvd, role, mask, w.budget_m, ckv)
+    torch.cuda.synchronize()
+    res = _host_results(ckv, H, Fh)
+    kept = _check_ragged(w, res, ref, role, mask, w.budget_m)
+    assert all(list(a) == list(b) for a, b in zip(kept, ref["kept"])), "tie band hit"
+    n = int(ref["tok_off"][-1])
+    assert np.array_equal(fkv.to_host(ckv.k)[:n], ref["k_c"])
+    assert np.array_equal(fkv.to_host(ckv.v)[:n], ref["v_c"])
+    out = G.run_attend(desc, qd, ckv, w.n_q, H, D, dtype)
+    G.check_output(G.host_f64(out), O.attend(q, ref["k_c"], ref["v_c"], ref["tok_off"]), dtype)
+
+
+@pytest.mark.parametrize("dtype,T,m,seed", [("bf16", 100, 3, 4), ("bf16", 64, 0, 5),
+                                            ("f32", 24, 2, 6)])
+def test_rolling_cache_rollout(dtype, T, m, seed):
+    """Six chunk steps with the cache carried over (RollingCache): every chunk's
+    kept frames, offsets, compacted rows and attention output against the
+    oracle's rollout; the cache size settles."""
+    import torch
+    D = 128 if dtype == "bf16" else 64
+    w = W.small_workload(name=f"roll_{dtype}", dtype=dtype, head_dim=D, tokens_per_frame=T,
+                         num_heads=4, hist_frames=9, budget_m=m, num_static=2, query_stride=4,
+                         seed=seed)
+    n_chunks = 6
+    ro = W.generate_rollout(w, n_chunks)
+    H, Fh, Fc = w.num_heads, w.hist_frames, w.cur_frames
+    ref = O.rollout(ro.q, ro.k, ro.v, ro.head_role, m, T, Fh, Fc, w.query_stride)
+    desc = fkv.desc_for(w)
+    rc = fkv.RollingCache(desc, ro.head_role, m)
+    k_all, v_all = fkv.to_device(ro.k), fkv.to_device(ro.v)
+    rows = []
+    for c in range(n_chunks):
+        q = fkv.to_device(ro.q[c])
+        lo, hi = (Fh + c * Fc) * T, (Fh + (c + 1) * Fc) * T
+        G.announce(f"rolling {dtype} chunk {c} T={T} m={m}")
+        if c == 0:
+            ckv = rc.step(q, k_all[lo:hi], v_all[lo:hi], window_k=k_all[:hi],
+                          window_v=v_all[:hi])
+        else:
+            ckv = rc.step(q, k_all[lo:hi], v_all[lo:hi])
+        torch.cuda.synchronize()
+        r = ref[c]
+        np.testing.assert_array_equal(rc.mask, r["mask"])
+        res = _host_results(ckv, H, Fh)
+        if c == 0:
+            r = dict(r, n_hist=np.full(H, Fh))
+        kept = _check_ragged(w, res, r, ro.head_role, r["mask"], m)
+        assert all(list(a) == list(b) for a, b in zip(kept, r["kept"])), f"chunk {c}: tie band"
+        n = int(r["tok_off"][-1])
+        assert rc.rows == n
+        assert np.array_equal(fkv.to_host(ckv.k)[:n], r["k_c"]), f"chunk {c}: K rows"
+        assert np.array_equal(fkv.to_host(ckv.v)[:n], r["v_c"]), f"chunk {c}: V rows"
+        assert [len(x) for x in rc.ids] == [len(x) for x in r["ids"]]
+        for h in range(H):
+            if ro.head_role[h] == O.STATIC:
+                assert rc.ids[h] == r["ids"][h]
+        out = G.run_attend(desc, q, ckv, w.n_q, H, D, dtype)
+        G.check_output(G.host_f64(out), O.attend(ro.q[c], r["k_c"], r["v_c"], r["tok_off"]),
+                       dtype)
+        rows.append(n)
+    assert rows[-1] == rows[-2] == rows[-3]
+
+
+@pytest.mark.parametrize("dtype,seed", [("bf16", 7), ("f32", 8)])
+def test_refresh_current(dtype, seed):
+    """Selection reused across denoising steps: after fkv_compress, a new
+    current chunk replaces the last F_c frames of every head bit for bit, and
+    attention sees it."""
+    import torch
+    D = 128 if dtype == "bf16" else 64
+    w = W.small_workload(name=f"refresh_{dtype}", dtype=dtype, head_dim=D, tokens_per_frame=90,
+                         num_heads=3, hist_frames=6, budget_m=3, seed=seed)
+    inp = W.generate_layer(w)
+    desc, ckv, (q, k, v), res = G.run_compress(w, inp)
+    T, Fh, Fc = w.tokens_per_frame, w.hist_frames, w.cur_frames
+    ref = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m, T,
+                     Fh, Fc, w.query_stride)
+    step2 = W.generate_layer(W.small_workload(name=f"refresh_{dtype}", dtype=dtype,
+                                              head_dim=D, tokens_per_frame=90, num_heads=3,
+                                              hist_frames=6, budget_m=3, seed=seed + 50))
+    cur_k, cur_v = step2.k[Fh * T:], step2.v[Fh * T:]
+    G.announce(f"fkv_refresh_current {dtype}")
+    fkv.fkv_refresh_current(desc, fkv.to_device(cur_k), fkv.to_device(cur_v), ckv)
+    torch.cuda.synchronize()
+    # the GPU's own selection (equal to the oracle's here) with the new chunk
+    kept = [np.array(res["seg_idx"][res["seg_off"][h]:res["seg_off"][h + 1]])
+            for h in range(w.num_heads)]
+    assert all(list(a) == list(b) for a, b in zip(kept, ref["kept"]))
+    k2, v2 = O.refresh_current(ref["k_c"], ref["v_c"], ref["tok_off"], cur_k, cur_v, T, Fc)
+    n = int(ref["tok_off"][-1])
+    assert np.array_equal(fkv.to_host(ckv.k)[:n], k2)
+    assert np.array_equal(fkv.to_host(ckv.v)[:n], v2)
+    q2 = fkv.to_device(step2.q)
+    out = G.run_attend(desc, q2, ckv, w.n_q, w.num_heads, D, dtype)
+    G.check_output(G.host_f64(out), O.attend(step2.q, k2, v2, ref["tok_off"]), dtype)
