@@ -45,6 +45,8 @@ def parse():
                     help="cycle over the workload's first N layers (own seeds, roles and "
                          "masks) instead of copies of layer 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rolling", action="store_true",
+                    help="skip the rolling-cache measurement")
     ap.add_argument("--profile-only", action="store_true",
                     help="run the timed loop only (for rocprofv3), print nothing else")
     ap.add_argument("--only", choices=["step", "compress", "attend", "dense", "copy"],
@@ -136,6 +138,65 @@ def measure(wname, args, fkv, torch, W):
                 compact_bytes=4.0 * kept * D * elt,
                 kept_frac_hist=(kept / w.num_heads / w.tokens_per_frame - w.cur_frames)
                 / max(w.hist_frames, 1))
+
+
+def measure_rolling(wname, args, fkv, torch, W, n_chunks=8):
+    """The cache carried across chunk steps (RollingCache): run n_chunks - 1
+    chunks so that every head's history has settled, then time, on the last
+    chunk's inputs, (a) a chunk step with fresh selection
+    (fkv_compress_ragged + fkv_attend) and (b) a later denoising step of the
+    same chunk with the selection reused (fkv_refresh_current + fkv_attend).
+    Memory: the settled cache against the plain window's K/V."""
+    w = W.WORKLOADS[wname]
+    ro = W.generate_rollout(w, n_chunks)
+    T, Fh, Fc, H = w.tokens_per_frame, w.hist_frames, w.cur_frames, w.num_heads
+    desc = fkv.desc_for(w)
+    rc = fkv.RollingCache(desc, ro.head_role, w.budget_m)
+    k_all, v_all = fkv.to_device(ro.k), fkv.to_device(ro.v)
+    qs = [fkv.to_device(q) for q in ro.q]
+    sizes = []
+    for c in range(n_chunks - 1):
+        lo, hi = (Fh + c * Fc) * T, (Fh + (c + 1) * Fc) * T
+        if c == 0:
+            rc.step(qs[0], k_all[lo:hi], v_all[lo:hi], window_k=k_all[:hi], window_v=v_all[:hi])
+        else:
+            rc.step(qs[c], k_all[lo:hi], v_all[lo:hi])
+        sizes.append(rc.rows)
+    torch.cuda.synchronize()
+    c = n_chunks - 1
+    lo, hi = (Fh + c * Fc) * T, (Fh + (c + 1) * Fc) * T
+    cur_k, cur_v, q = k_all[lo:hi], v_all[lo:hi], qs[c]
+    hist = rc.cache
+    hist_frames = [len(x) for x in rc.ids]
+    mask = rc._masks(rc.ids)
+    out_ckv = rc.bufs[rc.which ^ 1]
+    out = torch.empty((w.n_q, H, w.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def chunk_step(_):
+        fkv.fkv_compress_ragged(desc, q, hist, hist_frames, cur_k, cur_v, ro.head_role, mask,
+                                w.budget_m, out_ckv)
+        fkv.fkv_attend(desc, q, out_ckv, out, hist.attend_ws)
+
+    def reuse_step(_):
+        fkv.fkv_refresh_current(desc, cur_k, cur_v, out_ckv)
+        fkv.fkv_attend(desc, q, out_ckv, out, hist.attend_ws)
+
+    ms_chunk = time_loop(chunk_step, [None], args.steps, args.warmup, torch)
+    ms_reuse = time_loop(reuse_step, [None], args.steps, args.warmup, torch)
+    rows, _ = fkv.fkv_plan_ragged(desc, hist_frames, ro.head_role, mask, w.budget_m)
+    elt = 2 if w.dtype == "bf16" else 4
+    kv_bytes = lambda r: 2.0 * r * w.head_dim * elt
+    return {
+        "workload": w.name, "chunks_run": n_chunks,
+        "cache_rows_per_chunk": sizes + [rows],
+        "history_frames_per_head": hist_frames,
+        "ms_chunk_step_reselect": ms_chunk, "ms_step_selection_reused": ms_reuse,
+        "value_reselect": w.n_q / (ms_chunk * 1e-3),
+        "value_selection_reused": w.n_q / (ms_reuse * 1e-3),
+        "cache_bytes_settled": kv_bytes(rows),
+        "window_bytes_plain": kv_bytes(w.n_win * H),
+        "cache_reduction_vs_plain_window": 1.0 - rows / float(w.n_win * H),
+    }
 
 
 def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
@@ -260,6 +321,8 @@ def main():
             "attention_speedup_vs_full_kv": r2["ms_dense"] / r2["ms_attend"],
         }
         del r2
+    if w.dtype == "bf16" and not args.no_rolling and args.layers <= 1:
+        line["rolling"] = measure_rolling(w.name, args, fkv, torch, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:

@@ -304,13 +304,19 @@ class RollingCache:
     (seg_idx) and are recorded here as -1.
     """
 
-    def __init__(self, desc: FkvDesc, head_role, budget_m: int, device="cuda"):
+    def __init__(self, desc: FkvDesc, head_role, budget_m: int, device="cuda",
+                 static_cap=None):
         self.desc = desc
         self.role = np.asarray(head_role, dtype=np.uint8)
         self.m = int(budget_m)
         H, Fh, Fc = desc.num_heads, desc.hist_frames, desc.cur_frames
         if self.m > Fh - Fc:
             raise ValueError("a rolling cache needs budget_m <= hist_frames - cur_frames")
+        # Static heads keep at most as many frames as their pattern keeps in a
+        # plain window of F_h frames (and at most F_h - F_c).
+        if static_cap is None:
+            static_cap = int(fkv_roll_static_mask(list(range(Fh)), Fc, Fh).sum())
+        self.static_cap = min(int(static_cap), Fh - Fc)
         full = np.ones((H, Fh), dtype=np.uint8)
         self.bufs = [CompressedKV(desc, self.role, full, self.m, device=device,
                                   hist_frames=[Fh] * H) for _ in range(2)]
@@ -329,7 +335,7 @@ class RollingCache:
         mask = np.zeros((H, Fh), dtype=np.uint8)
         for h in range(H):
             if self.role[h] == 0:
-                mk = fkv_roll_static_mask(hist_ids[h], Fc, Fh - Fc)
+                mk = fkv_roll_static_mask(hist_ids[h], Fc, self.static_cap)
                 mask[h, :len(mk)] = mk
         return mask
 

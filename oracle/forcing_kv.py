@@ -352,9 +352,19 @@ def roll_static_keep(frame_ids: Sequence[int], cur_frames: int, cap: int) -> np.
     return mask
 
 
+def default_static_cap(hist_frames: int, cur_frames: int) -> int:
+    """Kept-frame cap of static heads in a rolling cache: as many frames as the
+    boundary pattern keeps in a plain window of F_h frames (the static
+    reduction stays constant in size, [S] 关键模块 › 2), and never more than
+    F_h - F_c, so that no history outgrows the window."""
+    n = sum(1 for f in range(hist_frames) if is_chunk_boundary(f, cur_frames))
+    return min(n, max(hist_frames - cur_frames, 0))
+
+
 def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray,
             head_role, budget_m: int, tokens_per_frame: int, hist_frames: int,
-            cur_frames: int, query_stride: int, scale: float = 0.0) -> List[Dict]:
+            cur_frames: int, query_stride: int, scale: float = 0.0,
+            static_cap: Optional[int] = None) -> List[Dict]:
     """Consecutive chunk steps of one layer with a rolling compressed cache.
 
     Chunk 0 compresses the plain window (frames [0, F_h + F_c) of the frame
@@ -363,8 +373,9 @@ def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray
     are gone for good, the finished chunk is appended.  Chunk c's current
     frames are [F_h + c F_c, F_h + (c + 1) F_c) of the store.  Static heads
     keep the boundary frames of their history (roll_static_keep, chunk 0
-    included) up to cap = F_h - F_c, so that no history outgrows F_h frames;
-    dynamic heads keep their top m, which must also be at most F_h - F_c.
+    included) up to static_cap (default_static_cap unless given, at most
+    F_h - F_c so that no history outgrows F_h frames); dynamic heads keep
+    their top m, which must also be at most F_h - F_c.
     Each result carries the static masks used (``mask`` [H, F_h]) and the
     absolute frame ids of every head's compacted frames (``ids``).
     """
@@ -372,6 +383,9 @@ def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray
     H = len(head_role)
     if budget_m > Fh - Fc:
         raise ValueError("a rolling cache needs m <= F_h - F_c")
+    cap = default_static_cap(Fh, Fc) if static_cap is None else static_cap
+    if cap > Fh - Fc:
+        raise ValueError("a rolling cache needs static_cap <= F_h - F_c")
     out = []
     for c in range(len(q_chunks)):
         first = Fh + c * Fc
@@ -379,7 +393,7 @@ def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray
         mask = np.zeros((H, Fh), dtype=np.uint8)
         for h in range(H):
             if head_role[h] != DYNAMIC:
-                mk = roll_static_keep(prev_ids[h], Fc, Fh - Fc)
+                mk = roll_static_keep(prev_ids[h], Fc, cap)
                 mask[h, :len(mk)] = mk
         if c == 0:
             n_win = (Fh + Fc) * T

@@ -192,3 +192,37 @@ def test_refresh_current(dtype, seed):
     q2 = fkv.to_device(step2.q)
     out = G.run_attend(desc, q2, ckv, w.n_q, w.num_heads, D, dtype)
     G.check_output(G.host_f64(out), O.attend(step2.q, k2, v2, ref["tok_off"]), dtype)
+
+
+def test_rolling_cache_480p_window():
+    """The 480P layer shape over three chunk steps: kept frames, offsets and
+    compacted rows exact against the oracle's rollout, attention on sampled
+    query rows (each computed by the oracle one by one)."""
+    import torch
+    w = W.WORKLOADS["480p_layer"]
+    n_chunks = 3
+    ro = W.generate_rollout(w, n_chunks)
+    H, Fh, Fc, T = w.num_heads, w.hist_frames, w.cur_frames, w.tokens_per_frame
+    ref = O.rollout(ro.q, ro.k, ro.v, ro.head_role, w.budget_m, T, Fh, Fc, w.query_stride)
+    desc = fkv.desc_for(w)
+    rc = fkv.RollingCache(desc, ro.head_role, w.budget_m)
+    k_all, v_all = fkv.to_device(ro.k), fkv.to_device(ro.v)
+    rows = np.random.default_rng(11).choice(w.n_q, 64, replace=False)
+    for c in range(n_chunks):
+        q = fkv.to_device(ro.q[c])
+        lo, hi = (Fh + c * Fc) * T, (Fh + (c + 1) * Fc) * T
+        G.announce(f"rolling 480p chunk {c}")
+        kw = dict(window_k=k_all[:hi], window_v=v_all[:hi]) if c == 0 else {}
+        ckv = rc.step(q, k_all[lo:hi], v_all[lo:hi], **kw)
+        torch.cuda.synchronize()
+        r = ref[c] if c else dict(ref[0], n_hist=np.full(H, Fh))
+        res = _host_results(ckv, H, Fh)
+        kept = _check_ragged(w, res, r, ro.head_role, r["mask"], w.budget_m)
+        assert all(list(a) == list(b) for a, b in zip(kept, r["kept"])), f"chunk {c}: tie band"
+        n = int(r["tok_off"][-1])
+        assert np.array_equal(fkv.to_host(ckv.k)[:n], r["k_c"])
+        assert np.array_equal(fkv.to_host(ckv.v)[:n], r["v_c"])
+        out = G.run_attend(desc, q, ckv, w.n_q, H, w.head_dim, w.dtype)
+        got = G.host_f64(out)[rows]
+        G.check_output(got, O.attend(ro.q[c], r["k_c"], r["v_c"], r["tok_off"], rows=rows),
+                       w.dtype)

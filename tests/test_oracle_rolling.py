@@ -101,6 +101,9 @@ def test_rollout_against_frame_store(m, num_static, seed):
     out = O.rollout(ro.q, ro.k, ro.v, ro.head_role, m, T, Fh, Fc, w.query_stride)
     kf = O.as_f64(ro.k)
     sc = O.logit_scale(w.head_dim)
+    # the plain window of 9 frames keeps 6 boundary frames (0, 2, 3, 5, 6, 8)
+    cap = O.default_static_cap(Fh, Fc)
+    assert cap == 6
     prev_ids = [list(range(Fh))] * w.num_heads
     sizes = []
     for c, r in enumerate(out):
@@ -117,7 +120,7 @@ def test_rollout_against_frame_store(m, num_static, seed):
                 assert list(r["kept"][h]) == list(O.select_dynamic(s, m))
             else:
                 want = [i for i, fid in enumerate(hist) if O.is_chunk_boundary(fid, Fc)]
-                while len(want) > Fh - Fc:
+                while len(want) > cap:
                     want.pop(next(j for j, i in enumerate(want) if hist[i] != 0))
                 assert list(r["kept"][h]) == want
             ids = r["ids"][h]
@@ -130,8 +133,10 @@ def test_rollout_against_frame_store(m, num_static, seed):
             assert np.array_equal(r["k_c"][lo:hi], store)
         prev_ids = r["ids"]
         sizes.append(int(r["tok_off"][-1]))
-    # steady state: a static head reaches F_h - F_c kept frames and stays
+    # steady state: static heads hold cap + F_c frames, dynamic m + F_c
     assert sizes[-1] == sizes[-2] == sizes[-3]
+    n_st = int((ro.head_role == O.STATIC).sum())
+    assert sizes[-1] == (n_st * (cap + Fc) + (w.num_heads - n_st) * (m + Fc)) * T
 
 
 def test_rollout_rejects_budget_beyond_capacity():
@@ -139,3 +144,9 @@ def test_rollout_rejects_budget_beyond_capacity():
     ro = W.generate_rollout(w, 2)
     with pytest.raises(ValueError):
         O.rollout(ro.q, ro.k, ro.v, ro.head_role, 4, 4, 6, 3, w.query_stride)
+
+
+def test_default_static_cap():
+    assert O.default_static_cap(18, 3) == 12          # the 480P / 1080P windows
+    assert O.default_static_cap(6, 3) == 3            # {0, 2, 3, 5} capped at F_h - F_c
+    assert O.default_static_cap(0, 3) == 0
