@@ -419,6 +419,99 @@ fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
   return ok();
 }
 
+fkv_status_t fkv_profile_workspace(const fkv_desc_t *desc, size_t *workspace_bytes) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!workspace_bytes) return fail(FKV_ERR_NULL, "workspace_bytes is NULL");
+  const int64_t n_q = (int64_t)desc->cur_frames * desc->tokens_per_frame;
+  const int64_t n_s = (n_q + desc->query_stride - 1) / desc->query_stride;
+  *workspace_bytes = (size_t)desc->num_heads * n_s * (desc->hist_frames + desc->cur_frames) *
+                     sizeof(float);
+  return ok();
+}
+
+fkv_status_t fkv_profile_heads(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                               float *mass_accum, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !mass_accum) return fail(FKV_ERR_NULL, "q, k_cache or mass_accum is NULL");
+  size_t need = 0;
+  fkv_profile_workspace(desc, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = desc->num_heads, Ft = desc->hist_frames + desc->cur_frames;
+  const int n_q = desc->cur_frames * desc->tokens_per_frame;
+  fkv::ScoreArgs sa;
+  sa.q = q;
+  sa.win = plain_window(desc, k_cache, k_cache);
+  sa.lse = reinterpret_cast<float *>(workspace);
+  sa.H = H;
+  sa.D = desc->head_dim;
+  sa.T = desc->tokens_per_frame;
+  sa.F_c = desc->cur_frames;
+  sa.F_tot = Ft;
+  sa.n_s = (n_q + desc->query_stride - 1) / desc->query_stride;
+  sa.stride = desc->query_stride;
+  sa.n_dyn = H;
+  sa.c = log2e_scale(*desc);
+  for (int h = 0; h < fkv::kMaxHeads; ++h) {
+    sa.dyn_heads[h] = h < H ? h : 0;
+    sa.fh[h] = desc->hist_frames;
+  }
+  hipError_t e = desc->dtype == FKV_BF16 ? fkv::launch_score_bf16(sa, s)
+                                         : fkv::launch_score_f32(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "scoring kernel launch");
+  fkv::ProfileArgs pa;
+  pa.lse = sa.lse;
+  pa.out = mass_accum;
+  pa.H = H;
+  pa.F_tot = Ft;
+  pa.n_s = sa.n_s;
+  e = fkv::launch_profile(pa, s);
+  if (e != hipSuccess) return hip_fail(e, "profiling kernel launch");
+  return ok();
+}
+
+fkv_status_t fkv_classify_heads(const fkv_desc_t *desc, const float *mass_sum, int32_t n_calls,
+                                float threshold, uint8_t *head_role, uint8_t *static_keep_mask,
+                                float *discontinuity) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  if (!mass_sum || !head_role || (!static_keep_mask && desc->hist_frames > 0))
+    return fail(FKV_ERR_NULL, "mass_sum, head_role or static_keep_mask is NULL");
+  if (n_calls < 1) return fail(FKV_ERR_SHAPE, "n_calls %d < 1", n_calls);
+  const int H = desc->num_heads, Fh = desc->hist_frames, Fc = desc->cur_frames;
+  const int Ft = Fh + Fc;
+  for (int h = 0; h < H; ++h) {
+    const float *row = mass_sum + (size_t)h * Ft;
+    double b_sum = 0, i_sum = 0;
+    int b_n = 0, i_n = 0;
+    for (int f = 0; f < Ft; ++f) {
+      const int pos = f % Fc;
+      const bool boundary = f == 0 || pos == 0 || pos == Fc - 1;
+      const double m = (double)row[f] / n_calls;
+      if (boundary) {
+        b_sum += m;
+        ++b_n;
+      } else {
+        i_sum += m;
+        ++i_n;
+      }
+    }
+    double disc = std::nan("");
+    if (b_n > 0 && i_n > 0 && i_sum > 0) disc = (b_sum / b_n) / (i_sum / i_n);
+    if (discontinuity) discontinuity[h] = (float)disc;
+    const bool is_static = disc >= (double)threshold;  // false for NaN
+    head_role[h] = is_static ? FKV_STATIC : FKV_DYNAMIC;
+    for (int f = 0; f < Fh; ++f)
+      static_keep_mask[(size_t)h * Fh + f] =
+          is_static && (double)row[f] / n_calls >= 1.0 / Ft ? 1 : 0;
+  }
+  return ok();
+}
+
 fkv_status_t fkv_attend_workspace(const fkv_desc_t *desc, size_t *workspace_bytes) {
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;

@@ -66,6 +66,15 @@ struct SelectArgs {
   int64_t tok_off_h[kMaxHeads + 1];
 };
 
+// Head profiling: per (head, window frame) mean mass over the sampled
+// queries, from the log-sum-exps of all heads (lse [H, n_s, F_tot]), added to
+// out [H, F_tot].
+struct ProfileArgs {
+  const float *lse;
+  float *out;
+  int32_t H, F_tot, n_s;
+};
+
 // Compaction.  With slots: one job per slot (head, window frame, rows).
 // Without (slots null): the current chunk only, slot s = (head s / F_c,
 // current frame s % F_c) going to the last F_c frames of the head's range in
@@ -99,6 +108,7 @@ struct AttendArgs {
 hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+hipError_t launch_profile(const ProfileArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int total_slots, hipStream_t s);
 // Bytes of partial-result buffer that the balanced bf16 attention schedule
 // needs on the current device (2 slots per workgroup, 2 workgroups per CU).

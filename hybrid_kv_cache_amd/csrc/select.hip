@@ -48,10 +48,12 @@ constexpr int kSelWaves = 4;
 // softmax over the head's window, whose first fh entries (the history) are
 // added to per-thread sums.  The sums are reduced over each wave with
 // shuffles and stored per wave in part[w][f].
+constexpr int kPartFrames = kMaxHistFrames + kMaxCurFrames;
+
 template <int FT>
 __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int ft,
-                                                  int fh, float (*part)[64], int tid, int lane,
-                                                  int wave) {
+                                                  int fh, float (*part)[kPartFrames], int tid,
+                                                  int lane, int wave) {
   float acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = 0.f;
@@ -74,7 +76,7 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
     for (int f = 0; f < FT; ++f) acc[f] += v[f] * inv;
   }
 #pragma unroll
-  for (int f = 0; f < FT && f < 64; ++f) {
+  for (int f = 0; f < FT && f < kPartFrames; ++f) {
     if (f < fh) {
       const float x = wave_sum(acc[f]);
       if (lane == 0) part[wave][f] = x;
@@ -83,7 +85,7 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
 }
 
 __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
-  __shared__ float part[kSelWaves][64];
+  __shared__ float part[kSelWaves][kPartFrames];
   __shared__ unsigned long long kept_bits_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
@@ -182,7 +184,33 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
   }
 }
 
+// Head profiling: the mean mass of every window frame of head blockIdx.x
+// over the sampled queries, added to out[h * F_tot + f] (accumulates over
+// calls; one workgroup per head, so the read-modify-write is unshared).
+__global__ __launch_bounds__(64 * kSelWaves) void profile_kernel(ProfileArgs a) {
+  __shared__ float part[kSelWaves][kPartFrames];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x;
+  const float *base = a.lse + (int64_t)h * a.n_s * a.F_tot;
+  if (a.F_tot <= 24)
+    accumulate_masses<24>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane, wave);
+  else
+    accumulate_masses<72>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane, wave);
+  __syncthreads();
+  if (tid < a.F_tot) {
+    float sum = part[0][tid];
+#pragma unroll
+    for (int w = 1; w < kSelWaves; ++w) sum += part[w][tid];
+    a.out[(int64_t)h * a.F_tot + tid] += sum / (float)a.n_s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_profile(const ProfileArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(profile_kernel, dim3(a.H), dim3(64 * kSelWaves), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(select_kernel, dim3(a.H), dim3(64 * kSelWaves), 0, s, a);

@@ -25,7 +25,8 @@ FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
 EXPORTED = ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
-            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_attend_workspace",
+            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_profile_workspace",
+            "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
             "fkv_attend", "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
 
 
@@ -71,11 +72,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, P, P, P, I32, ctypes.POINTER(FkvCkv), P, SZ, P]
     lib.fkv_refresh_current.argtypes = [ctypes.POINTER(FkvDesc), P, P, ctypes.POINTER(FkvCkv), P]
     lib.fkv_roll_static_mask.argtypes = [I32, P, I32, I32, P]
+    lib.fkv_profile_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
+    lib.fkv_profile_heads.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, SZ, P]
+    lib.fkv_classify_heads.argtypes = [ctypes.POINTER(FkvDesc), P, I32, ctypes.c_float, P, P, P]
     lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
     for name in ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
-                 "fkv_refresh_current", "fkv_roll_static_mask", "fkv_attend_workspace",
+                 "fkv_refresh_current", "fkv_roll_static_mask", "fkv_profile_workspace",
+                 "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
                  "fkv_attend", "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fkv_status_str.argtypes = [ctypes.c_int]
@@ -226,6 +231,36 @@ def fkv_refresh_current(desc: FkvDesc, cur_k, cur_v, ckv: CompressedKV, stream=N
     s = ckv.struct()
     _check(lib.fkv_refresh_current(ctypes.byref(desc), _ptr(cur_k), _ptr(cur_v), ctypes.byref(s),
                                    _stream(stream)))
+
+
+def fkv_profile_workspace(desc: FkvDesc) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.fkv_profile_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def fkv_profile_heads(desc: FkvDesc, q, k_cache, mass_accum, workspace, stream=None) -> None:
+    """Adds this sample's per-(head, frame) mean masses to mass_accum [H, F_tot]
+    (a device fp32 tensor)."""
+    lib = load()
+    _check(lib.fkv_profile_heads(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(mass_accum),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def fkv_classify_heads(desc: FkvDesc, mass_sum: np.ndarray, n_calls: int, threshold: float):
+    """Host labels from summed masses: (head_role, static_keep_mask, discontinuity)."""
+    lib = load()
+    H, Fh = desc.num_heads, desc.hist_frames
+    m = np.ascontiguousarray(mass_sum, dtype=np.float32)
+    role = np.zeros(H, dtype=np.uint8)
+    mask = np.zeros((H, max(Fh, 1)), dtype=np.uint8)
+    disc = np.zeros(H, dtype=np.float32)
+    _check(lib.fkv_classify_heads(ctypes.byref(desc), m.ctypes.data, int(n_calls),
+                                  float(threshold), role.ctypes.data, mask.ctypes.data,
+                                  disc.ctypes.data))
+    return role, mask[:, :Fh], disc
 
 
 def fkv_attend_workspace(desc: FkvDesc) -> int:

@@ -278,6 +278,43 @@ def generate_rollout(w: Workload, n_chunks: int, seed: Optional[int] = None) -> 
                          static_keep_mask=np.ascontiguousarray(mask, dtype=np.uint8))
 
 
+def generate_profile_sample(w: Workload, sample: int = 0, strength: float = 4.0) -> LayerInputs:
+    """A warm-up sample for head profiling: generate_layer's recipe with the
+    seed of layer `sample` for the content, the head roles of layer 0 (roles
+    belong to the model, not to the sample), plus a positional signature on
+    the static heads: a unit direction u_h (one per head, from its own
+    seeded generator) is added, times `strength`, to every query of the head
+    and to the keys of its boundary frames (the sink and the first and last
+    frame of every aligned chunk of F_c frames, current chunk included), so
+    that these heads attend to chunk starts and ends as the pages describe
+    static heads doing.  Dynamic heads are left as generate_layer makes them."""
+    base = generate_layer(w, sample)
+    base.head_role = generate_layer(small_copy(w), 0).head_role
+    H, D, T, F = w.num_heads, w.head_dim, w.tokens_per_frame, w.frames
+    rng = np.random.Generator(np.random.PCG64(w.seed(sample) + 7919))
+    u = rng.standard_normal((H, D)).astype(np.float32)
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    q = base.as_f32("q").copy()
+    k = base.as_f32("k").copy()
+    Fc = w.cur_frames
+    boundary = [f for f in range(F) if f == 0 or f % Fc in (0, Fc - 1)]
+    for h in range(H):
+        if base.head_role[h] != STATIC:
+            continue
+        q[:, h] += np.float32(strength) * u[h]
+        for f in boundary:
+            k[f * T:(f + 1) * T, h] += np.float32(strength) * u[h]
+    conv = (lambda a: round_to_bf16_bits(a)) if w.dtype == "bf16" else (lambda a: a)
+    base.q, base.k = conv(np.ascontiguousarray(q)), conv(np.ascontiguousarray(k))
+    return base
+
+
+def small_copy(w: Workload) -> Workload:
+    """The same workload with one-token frames (same seeds and head roles):
+    cheap to generate when only the role draw is wanted."""
+    return dataclasses.replace(w, tokens_per_frame=1, dtype="f32")
+
+
 def iter_layers(w: Workload, layers: Optional[List[int]] = None) -> Iterator[LayerInputs]:
     for l in (range(w.num_layers) if layers is None else layers):
         yield generate_layer(w, l)

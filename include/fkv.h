@@ -167,6 +167,37 @@ fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, cons
 fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
                                   int32_t cur_frames, int32_t cap, uint8_t *mask);
 
+/* ---- Offline head profiling ([S] 关键模块 1) --------------------------------
+ * Run on a few warm-up samples before inference; produces the head labels and
+ * static keep masks that fkv_plan / fkv_compress take. */
+
+/* Device workspace bytes fkv_profile_heads needs: H * n_s * (F_h + F_c) fp32,
+ * n_s = ceil(Nq / query_stride). */
+fkv_status_t fkv_profile_workspace(const fkv_desc_t *desc, size_t *workspace_bytes);
+
+/* Attention mass by frame for every head: for each head h and window frame f,
+ * the mean over the sampled queries (rows 0, s, 2s, ...; s = desc->query_stride,
+ * 1 for all) of the softmax mass on frame f (softmax over the whole window,
+ * scale * q.k logits), ADDED to mass_accum[h * (F_h + F_c) + f] (device fp32,
+ * the caller zeroes it once and sums over samples / steps).  q, k_cache as for
+ * fkv_compress (v is not needed). */
+fkv_status_t fkv_profile_heads(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                               float *mass_accum, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Host: labels from the summed masses (host copy of mass_accum, n_calls
+ * calls).  Chunk discontinuity of head h = mean mass of its boundary frames
+ * (window frame f is one when f == 0 or f % F_c is 0 or F_c - 1: the sink and
+ * the first and last frame of every aligned chunk) over the mean mass of the
+ * others (NaN when there are no others or they get no mass).  The head is
+ * static when discontinuity >= threshold (never for NaN), else dynamic; a
+ * static head's mask row marks the history frames whose mean mass is at
+ * least 1 / (F_h + F_c), a dynamic head's row is 0.  discontinuity[H] may be
+ * NULL. */
+fkv_status_t fkv_classify_heads(const fkv_desc_t *desc, const float *mass_sum, int32_t n_calls,
+                                float threshold, uint8_t *head_role, uint8_t *static_keep_mask,
+                                float *discontinuity);
+
 /* Bytes of the optional attention workspace for the current HIP device: the
  * bf16 attention can then split its work into equal parts, one per resident
  * workgroup (two per compute unit), whatever the number of (head, 128-query)

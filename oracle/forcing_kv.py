@@ -412,6 +412,54 @@ def rollout(q_chunks: Sequence[np.ndarray], k_all: np.ndarray, v_all: np.ndarray
     return out
 
 
+def profile_masses(q, k, tokens_per_frame: int, query_stride: int = 1,
+                   scale: float = 0.0) -> np.ndarray:
+    """Offline head profiling ([S] 关键模块 › 1): the attention mass every
+    head puts on every window frame, averaged over the current chunk's
+    queries (rows 0, s, 2s, ...; s = 1 takes them all), softmax over the
+    whole window.  Returns [H, F_total]; each row sums to 1."""
+    q = as_f64(q)
+    k = as_f64(k)
+    H, D = q.shape[1], q.shape[2]
+    sc = logit_scale(D, scale)
+    return np.stack([frame_masses(q[:, h, :], k[:, h, :], tokens_per_frame, query_stride,
+                                  sc).mean(axis=0) for h in range(H)])
+
+
+def chunk_discontinuity(mass_row: np.ndarray, cur_frames: int) -> float:
+    """Reading of the pages' chunk-discontinuity indicator at frame
+    granularity ([S] 关键模块 › 1: static heads concentrate on the chunk's start
+    and end positions): the mean mass of the boundary frames (sink, first and
+    last frame of each aligned F_c-frame chunk; window frame f has id f) over
+    the mean mass of the other frames.  NaN when every frame is a boundary
+    (F_c <= 2) or the other frames get no mass."""
+    b = np.array([is_chunk_boundary(f, cur_frames) for f in range(len(mass_row))])
+    if b.all() or not (~b).any():
+        return float("nan")
+    inner = float(np.mean(mass_row[~b]))
+    return float(np.mean(mass_row[b]) / inner) if inner > 0 else float("nan")
+
+
+def classify_heads(mass_sum: np.ndarray, n_calls: int, hist_frames: int, cur_frames: int,
+                   threshold: float):
+    """Head labels from profiled masses (summed over n_calls calls): a head
+    is static when its chunk discontinuity is at least `threshold` (NaN is
+    not), else dynamic.  A static head's keep mask marks the history frames
+    whose mean mass is at least the uniform share 1 / F_total ([S] 关键模块 › 2:
+    the fixed positions that matter, frozen after profiling).
+    Returns (head_role [H] uint8, static_keep_mask [H, F_h] uint8, disc [H])."""
+    mass = np.asarray(mass_sum, dtype=np.float64) / n_calls
+    H, F_tot = mass.shape
+    role = np.full(H, DYNAMIC, dtype=np.uint8)
+    mask = np.zeros((H, hist_frames), dtype=np.uint8)
+    disc = np.array([chunk_discontinuity(mass[h], cur_frames) for h in range(H)])
+    for h in range(H):
+        if disc[h] >= threshold:
+            role[h] = STATIC
+            mask[h] = mass[h, :hist_frames] >= 1.0 / F_tot
+    return role, mask, disc
+
+
 def cutoff_band(score_row: np.ndarray, budget_m: int, rel: float = TIE_REL):
     """Frames whose membership in the top-m set is decided by a near tie.
 

@@ -1,0 +1,60 @@
+"""GPU parity of the head-profiling statistics (fkv_profile_heads) against
+the CPU oracle, and the labels they lead to."""
+import numpy as np
+import pytest
+
+from hybrid_kv_cache_amd import fkv
+from hybrid_kv_cache_amd import workloads as W
+from oracle import forcing_kv as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.require_gpu()
+
+
+def _profile(w, samples):
+    import torch
+    desc = fkv.desc_for(w)
+    ws = torch.empty(fkv.fkv_profile_workspace(desc), dtype=torch.uint8, device="cuda")
+    acc = torch.zeros((w.num_heads, w.frames), dtype=torch.float32, device="cuda")
+    ref = np.zeros((w.num_heads, w.frames))
+    for inp in samples:
+        q, k = fkv.to_device(inp.q), fkv.to_device(inp.k)
+        G.announce(f"fkv_profile_heads {w.name} H={w.num_heads} T={w.tokens_per_frame} "
+                   f"s={w.query_stride}")
+        fkv.fkv_profile_heads(desc, q, k, acc, ws)
+        ref += O.profile_masses(inp.q, inp.k, w.tokens_per_frame, w.query_stride)
+    torch.cuda.synchronize()
+    return desc, fkv.to_host(acc), ref
+
+
+@pytest.mark.parametrize("dtype,T,s,seed", [("bf16", 100, 1, 31), ("bf16", 37, 3, 32),
+                                            ("f32", 40, 1, 33)])
+def test_profile_masses_and_labels(dtype, T, s, seed):
+    D = 128 if dtype == "bf16" else 64
+    w = W.small_workload(name=f"profile_{dtype}", dtype=dtype, head_dim=D, tokens_per_frame=T,
+                         num_heads=6, hist_frames=9, num_static=3, query_stride=s, seed=seed)
+    samples = [W.generate_profile_sample(w, i) for i in range(2)]
+    desc, got, ref = _profile(w, samples)
+    np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-6)
+    np.testing.assert_allclose(got.sum(axis=1), 2.0, rtol=1e-4)
+    # labels: the library's host rule on the GPU masses equals the oracle's
+    # rule on the same masses, and both recover the planted static heads
+    role, mask, disc = fkv.fkv_classify_heads(desc, got, 2, 2.0)
+    r2, m2, d2 = O.classify_heads(got.astype(np.float64), 2, w.hist_frames, w.cur_frames, 2.0)
+    assert np.array_equal(role, r2) and np.array_equal(mask, m2)
+    assert np.array_equal(role, samples[0].head_role)
+
+
+def test_profile_480p_layer_shape():
+    """The 480P window (12 heads, T = 1560, 21 frames), every 16th query."""
+    w = W.WORKLOADS["480p_layer"]
+    samples = [W.generate_profile_sample(w, 0)]
+    desc, got, ref = _profile(w, samples)
+    np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-6)
+    role, _, _ = fkv.fkv_classify_heads(desc, got, 1, 2.0)
+    assert np.array_equal(role, samples[0].head_role)
