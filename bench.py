@@ -199,6 +199,25 @@ def measure_rolling(wname, args, fkv, torch, W, n_chunks=8):
     }
 
 
+def measure_profile(wname, args, fkv, torch, W, stride=1):
+    """Head profiling over every query of one warm-up sample
+    (fkv_profile_heads, query stride 1): time per call and the score
+    product's rate, 2 Nq D N_win H FLOP."""
+    w = W.WORKLOADS[wname]
+    inp = W.generate_profile_sample(w, 0)
+    desc = fkv.make_desc(w.num_heads, w.head_dim, w.tokens_per_frame, w.hist_frames,
+                         w.cur_frames, stride, w.dtype)
+    q, k = fkv.to_device(inp.q), fkv.to_device(inp.k)
+    ws = torch.empty(fkv.fkv_profile_workspace(desc), dtype=torch.uint8, device="cuda")
+    acc = torch.zeros((w.num_heads, w.frames), dtype=torch.float32, device="cuda")
+    ms = time_loop(lambda _: fkv.fkv_profile_heads(desc, q, k, acc, ws), [None],
+                   max(args.steps // 4, 3), 2, torch)
+    n_s = -(-w.n_q // stride)
+    flop = 2.0 * n_s * w.head_dim * w.n_win * w.num_heads
+    return {"workload": w.name, "query_stride": stride, "ms_per_sample": ms,
+            "score_tflops": flop / (ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
     """The oracle as it stands, timed on this host over the whole layer
     (scoring, selection, compaction and attention of every query row),
@@ -323,6 +342,7 @@ def main():
         del r2
     if w.dtype == "bf16" and not args.no_rolling and args.layers <= 1:
         line["rolling"] = measure_rolling(w.name, args, fkv, torch, W)
+        line["head_profiling"] = measure_profile(w.name, args, fkv, torch, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:
