@@ -460,6 +460,90 @@ def classify_heads(mass_sum: np.ndarray, n_calls: int, hist_frames: int, cur_fra
     return role, mask, disc
 
 
+# ---- token-granular variant -------------------------------------------------
+
+def static_token_keep(hist_frames: int, tokens_per_frame: int, cur_frames: int,
+                      sink_frames: int, boundary_tokens: int) -> np.ndarray:
+    """Token-granular static pattern ([S] 关键模块 › 1 and 2: static heads attend
+    to the start and end tokens of a chunk, and keep those positions): the
+    tokens of the first sink_frames history frames, plus the first and the last
+    boundary_tokens tokens of every aligned history chunk of F_c frames (a
+    trailing partial chunk included).  Sorted history token indices."""
+    T, Fh = tokens_per_frame, hist_frames
+    n = Fh * T
+    keep = np.zeros(n, dtype=bool)
+    keep[:min(sink_frames, Fh) * T] = True
+    L = boundary_tokens
+    for start in range(0, Fh, cur_frames):
+        lo, hi = start * T, min(start + cur_frames, Fh) * T
+        keep[lo:min(lo + L, hi)] = True
+        keep[max(hi - L, lo):hi] = True
+    return np.flatnonzero(keep).astype(np.int64)
+
+
+def participative_scores(q_h: np.ndarray, k_cand: np.ndarray, query_stride: int) -> np.ndarray:
+    """Importance of each candidate token j of one head: the summed dot products
+    with the sampled current-chunk queries, phi_j = sum_r q_r . k_j (the
+    participative rule on the Deep Forcing page, 3.1 动态token筛选算法: each
+    candidate scored by the attention logits the recent queries give it;
+    here the recent queries are the strided sample of the current chunk).
+    Written as the double sum, float64."""
+    rows = sampled_query_rows(q_h.shape[0], query_stride)
+    return (as_f64(q_h)[rows] @ as_f64(k_cand).T).sum(axis=0)
+
+
+def select_top_tokens(phi: np.ndarray, budget: int) -> np.ndarray:
+    """The min(C, n) candidates ranked first by (phi descending, index
+    ascending), returned in ascending order (Top-C selection)."""
+    n = len(phi)
+    c = min(max(budget, 0), n)
+    order = sorted(range(n), key=lambda j: (-phi[j], j))
+    return np.array(sorted(order[:c]), dtype=np.int64)
+
+
+def compress_tokens(q, k, v, head_role, tokens_per_frame: int, hist_frames: int,
+                    cur_frames: int, query_stride: int, sink_frames: int, recent_frames: int,
+                    budget_tokens: int, boundary_tokens: int) -> Dict[str, object]:
+    """Token-granular compression of one layer (plain window).
+
+    Static head: static_token_keep.  Dynamic head: the history is cut into a
+    sink (first sink_frames frames, kept), a recent zone (last recent_frames
+    frames, kept) and the candidates between them, of which the top
+    budget_tokens by participative score are kept ([Deep Forcing page] 3.1:
+    Sink / Recent / Candidate zones, Top-C with C the remaining budget).
+    Compacted rows per head: kept history tokens ascending, then the current
+    chunk.  Returns src (per head, the window token index of every compacted
+    row), k_c, v_c, tok_off and phi (per dynamic head, candidate scores).
+    """
+    T, Fh, Fc = tokens_per_frame, hist_frames, cur_frames
+    H = len(head_role)
+    n_hist = Fh * T
+    s_tok = min(sink_frames, Fh) * T
+    r_tok = min(recent_frames, max(Fh - min(sink_frames, Fh), 0)) * T
+    cand_lo, cand_hi = s_tok, n_hist - r_tok
+    src, phi = [], {}
+    for h in range(H):
+        if head_role[h] == DYNAMIC:
+            p = participative_scores(q[:, h], k[cand_lo:cand_hi, h], query_stride)
+            phi[h] = p
+            sel = select_top_tokens(p, budget_tokens) + cand_lo
+            hist = np.concatenate([np.arange(0, s_tok), sel, np.arange(cand_hi, n_hist)])
+        else:
+            hist = static_token_keep(Fh, T, Fc, sink_frames, boundary_tokens)
+        src.append(np.concatenate([hist, np.arange(n_hist, n_hist + Fc * T)]).astype(np.int64))
+    tok_off = np.zeros(H + 1, dtype=np.int64)
+    for h in range(H):
+        tok_off[h + 1] = tok_off[h] + len(src[h])
+    D = k.shape[2]
+    k_c = np.empty((int(tok_off[H]), D), dtype=k.dtype)
+    v_c = np.empty((int(tok_off[H]), D), dtype=v.dtype)
+    for h in range(H):
+        k_c[tok_off[h]:tok_off[h + 1]] = k[src[h], h]
+        v_c[tok_off[h]:tok_off[h + 1]] = v[src[h], h]
+    return dict(src=src, k_c=k_c, v_c=v_c, tok_off=tok_off, phi=phi,
+                cand=(cand_lo, cand_hi))
+
+
 def cutoff_band(score_row: np.ndarray, budget_m: int, rel: float = TIE_REL):
     """Frames whose membership in the top-m set is decided by a near tie.
 
