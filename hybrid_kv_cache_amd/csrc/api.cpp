@@ -301,6 +301,89 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   return ok();
 }
 
+// ---- token-granular plan ---------------------------------------------------
+
+struct TokenPlan {
+  int H, D, T, Fh, Fc, n_q, n_hist, n_cur, sink_tok, recent_tok, cand_lo, cand_hi, n_cand;
+  int budget, boundary, n_dyn, max_rows;
+  int dyn_heads[fkv::kMaxHeads];
+  int dyn_index[fkv::kMaxHeads];
+  int64_t tok_off[fkv::kMaxHeads + 1];
+  size_t ws_qsum_off, ws_phi_off, ws_src_off, ws_bytes;
+};
+
+// History tokens a static head keeps: the sink tokens and both ends of every
+// aligned chunk, as a union of at most two intervals per chunk.
+int64_t static_token_count(int n_hist, int chunk, int sink_tok, int L) {
+  int64_t count = 0;
+  for (int lo = 0; lo < n_hist; lo += chunk) {
+    const int hi = lo + chunk < n_hist ? lo + chunk : n_hist;
+    int e1 = lo + L < hi ? lo + L : hi;                       // [lo, e1): first L (and sink)
+    const int sink_end = sink_tok < hi ? sink_tok : hi;
+    if (sink_end > e1) e1 = sink_end;
+    const int s2 = hi - L > lo ? hi - L : lo;                 // [s2, hi): last L
+    const int overlap = e1 > s2 ? e1 - s2 : 0;
+    count += (e1 - lo) + (hi - s2) - overlap;
+  }
+  return count;
+}
+
+fkv_status_t make_token_plan(const fkv_desc_t *d, const fkv_token_cfg_t *cfg,
+                             const uint8_t *role, TokenPlan *p) {
+  fkv_status_t st = check_desc(d);
+  if (st != FKV_OK) return st;
+  if (!cfg || !role) return fail(FKV_ERR_NULL, "cfg or head_role is NULL");
+  if (cfg->sink_frames < 0 || cfg->recent_frames < 0 || cfg->boundary_tokens < 0)
+    return fail(FKV_ERR_SHAPE, "sink_frames, recent_frames and boundary_tokens must be >= 0");
+  if (cfg->budget_tokens < 0) return fail(FKV_ERR_BUDGET, "budget_tokens %d < 0",
+                                          cfg->budget_tokens);
+  p->H = d->num_heads;
+  p->D = d->head_dim;
+  p->T = d->tokens_per_frame;
+  p->Fh = d->hist_frames;
+  p->Fc = d->cur_frames;
+  p->n_q = p->Fc * p->T;
+  p->n_hist = p->Fh * p->T;
+  p->n_cur = p->Fc * p->T;
+  const int sink_f = cfg->sink_frames < p->Fh ? cfg->sink_frames : p->Fh;
+  const int rest = p->Fh - sink_f;
+  const int recent_f = cfg->recent_frames < rest ? cfg->recent_frames : rest;
+  p->sink_tok = sink_f * p->T;
+  p->recent_tok = recent_f * p->T;
+  p->cand_lo = p->sink_tok;
+  p->cand_hi = p->n_hist - p->recent_tok;
+  p->n_cand = p->cand_hi - p->cand_lo;
+  p->budget = cfg->budget_tokens;
+  p->boundary = cfg->boundary_tokens;
+  p->n_dyn = 0;
+  p->max_rows = 0;
+  p->tok_off[0] = 0;
+  const int64_t dyn_kept = (int64_t)p->sink_tok + (p->budget < p->n_cand ? p->budget : p->n_cand) +
+                           p->recent_tok;
+  const int64_t st_kept = static_token_count(p->n_hist, p->Fc * p->T, p->sink_tok, p->boundary);
+  for (int h = 0; h < p->H; ++h) {
+    if (role[h] != FKV_STATIC && role[h] != FKV_DYNAMIC)
+      return fail(FKV_ERR_SHAPE, "head_role[%d] = %d is neither static (0) nor dynamic (1)", h,
+                  role[h]);
+    p->dyn_index[h] = -1;
+    if (role[h] == FKV_DYNAMIC) {
+      p->dyn_index[h] = p->n_dyn;
+      p->dyn_heads[p->n_dyn++] = h;
+    }
+    const int64_t rows = (role[h] == FKV_DYNAMIC ? dyn_kept : st_kept) + p->n_cur;
+    p->tok_off[h + 1] = p->tok_off[h] + rows;
+    if (rows > p->max_rows) p->max_rows = (int)rows;
+  }
+  for (int h = p->n_dyn; h < fkv::kMaxHeads; ++h) p->dyn_heads[h] = 0;
+  for (int h = p->H; h < fkv::kMaxHeads; ++h) p->dyn_index[h] = -1;
+  for (int h = p->H + 1; h <= fkv::kMaxHeads; ++h) p->tok_off[h] = p->tok_off[p->H];
+  p->ws_qsum_off = 0;
+  p->ws_phi_off = align256((size_t)p->n_dyn * p->D * sizeof(float));
+  p->ws_src_off = p->ws_phi_off + align256((size_t)p->n_dyn * p->n_cand * sizeof(float));
+  p->ws_bytes = p->ws_src_off + align256((size_t)p->tok_off[p->H] * sizeof(int32_t));
+  return FKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -416,6 +499,74 @@ fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
       --kept;
     }
   }
+  return ok();
+}
+
+fkv_status_t fkv_plan_tokens(const fkv_desc_t *desc, const fkv_token_cfg_t *cfg,
+                             const uint8_t *head_role, int64_t *kept_tokens,
+                             size_t *workspace_bytes) {
+  TokenPlan p;
+  fkv_status_t st = make_token_plan(desc, cfg, head_role, &p);
+  if (st != FKV_OK) return st;
+  if (kept_tokens) *kept_tokens = p.tok_off[p.H];
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+fkv_status_t fkv_compress_tokens(const fkv_desc_t *desc, const fkv_token_cfg_t *cfg,
+                                 const void *q, const void *k_cache, const void *v_cache,
+                                 const uint8_t *head_role, const fkv_ckv_t *out,
+                                 int32_t *row_src, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  TokenPlan p;
+  fkv_status_t st = make_token_plan(desc, cfg, head_role, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  if (!out || !out->k || !out->v || !out->tok_off)
+    return fail(FKV_ERR_NULL, "a compressed-cache buffer (k, v, tok_off) is NULL");
+  if (out->cap_tokens < p.tok_off[p.H])
+    return fail(FKV_ERR_CAPACITY, "cap_tokens %lld < %lld rows needed",
+                (long long)out->cap_tokens, (long long)p.tok_off[p.H]);
+  if (!workspace || workspace_bytes < p.ws_bytes)
+    return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // The plan's offsets reach the device as kernel arguments; the selection
+  // kernel writes them to out->tok_off.
+  char *ws = reinterpret_cast<char *>(workspace);
+  fkv::TokenArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_out = reinterpret_cast<char *>(out->k);
+  a.v_out = reinterpret_cast<char *>(out->v);
+  a.src = row_src ? row_src : reinterpret_cast<int32_t *>(ws + p.ws_src_off);
+  a.qsum = reinterpret_cast<float *>(ws + p.ws_qsum_off);
+  a.phi = reinterpret_cast<float *>(ws + p.ws_phi_off);
+  a.H = p.H;
+  a.D = p.D;
+  a.elt = elt_bytes(desc->dtype);
+  a.T = p.T;
+  a.F_c = p.Fc;
+  a.n_q = p.n_q;
+  a.stride = desc->query_stride;
+  a.n_hist = p.n_hist;
+  a.n_cur = p.n_cur;
+  a.sink_tok = p.sink_tok;
+  a.recent_tok = p.recent_tok;
+  a.cand_lo = p.cand_lo;
+  a.cand_hi = p.cand_hi;
+  a.n_cand = p.n_cand;
+  a.budget = p.budget;
+  a.boundary = p.boundary;
+  a.n_dyn = p.n_dyn;
+  a.max_rows = p.max_rows;
+  a.tok_off_out = out->tok_off;
+  std::memcpy(a.dyn_heads, p.dyn_heads, sizeof(a.dyn_heads));
+  std::memcpy(a.dyn_index, p.dyn_index, sizeof(a.dyn_index));
+  std::memcpy(a.tok_off_h, p.tok_off, sizeof(a.tok_off_h));
+  hipError_t e = fkv::launch_tokens(a, s);
+  if (e != hipSuccess) return hip_fail(e, "token compression kernel launch");
   return ok();
 }
 

@@ -75,6 +75,24 @@ struct ProfileArgs {
   int32_t H, F_tot, n_s;
 };
 
+// Token-granular compression (see tokens.hip).  History tokens of head h are
+// t = 0 .. n_hist - 1 (frame-major), the current chunk n_hist .. n_hist + n_cur - 1;
+// window row of token t, head h: (t * H + h) * D elements of q's element type.
+struct TokenArgs {
+  const void *q, *k, *v;    // [Nq, H, D], [N_win, H, D] x2
+  char *k_out, *v_out;      // [rows, D]
+  int32_t *src;             // [rows]: window token index of each compacted row
+  int64_t *tok_off_out;     // [H + 1]: offsets written for attention
+  float *qsum;              // [n_dyn, D]
+  float *phi;               // [n_dyn, n_cand]
+  int32_t H, D, elt, T, F_c, n_q, stride;
+  int32_t n_hist, n_cur, sink_tok, recent_tok, cand_lo, cand_hi, n_cand, budget, boundary;
+  int32_t n_dyn, max_rows;
+  int32_t dyn_heads[kMaxHeads];
+  int32_t dyn_index[kMaxHeads];   // -1: static
+  int64_t tok_off_h[kMaxHeads + 1];
+};
+
 // Compaction.  With slots: one job per slot (head, window frame, rows).
 // Without (slots null): the current chunk only, slot s = (head s / F_c,
 // current frame s % F_c) going to the last F_c frames of the head's range in
@@ -109,6 +127,7 @@ hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 hipError_t launch_profile(const ProfileArgs &a, hipStream_t s);
+hipError_t launch_tokens(const TokenArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int total_slots, hipStream_t s);
 // Bytes of partial-result buffer that the balanced bf16 attention schedule
 // needs on the current device (2 slots per workgroup, 2 workgroups per CU).

@@ -25,7 +25,8 @@ FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
 EXPORTED = ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
-            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_profile_workspace",
+            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
+            "fkv_compress_tokens", "fkv_profile_workspace",
             "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
             "fkv_attend", "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
 
@@ -53,6 +54,11 @@ class FkvError(RuntimeError):
 _lib = None
 
 
+class FkvTokenCfg(ctypes.Structure):
+    _fields_ = [("sink_frames", ctypes.c_int32), ("recent_frames", ctypes.c_int32),
+                ("budget_tokens", ctypes.c_int32), ("boundary_tokens", ctypes.c_int32)]
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libfkv.so (once).  Raises if it is missing."""
     global _lib
@@ -72,6 +78,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, P, P, P, I32, ctypes.POINTER(FkvCkv), P, SZ, P]
     lib.fkv_refresh_current.argtypes = [ctypes.POINTER(FkvDesc), P, P, ctypes.POINTER(FkvCkv), P]
     lib.fkv_roll_static_mask.argtypes = [I32, P, I32, I32, P]
+    lib.fkv_plan_tokens.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(FkvTokenCfg), P,
+                                    ctypes.POINTER(I64), ctypes.POINTER(SZ)]
+    lib.fkv_compress_tokens.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(FkvTokenCfg), P,
+                                        P, P, P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_profile_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_profile_heads.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, SZ, P]
     lib.fkv_classify_heads.argtypes = [ctypes.POINTER(FkvDesc), P, I32, ctypes.c_float, P, P, P]
@@ -79,7 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
     for name in ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
-                 "fkv_refresh_current", "fkv_roll_static_mask", "fkv_profile_workspace",
+                 "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
+            "fkv_compress_tokens", "fkv_profile_workspace",
                  "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
                  "fkv_attend", "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
@@ -171,9 +182,11 @@ class CompressedKV:
     With hist_frames (per-head history lengths), sized for fkv_compress_ragged."""
 
     def __init__(self, desc: FkvDesc, head_role, static_keep_mask, budget_m: int,
-                 device="cuda", with_scores: bool = True, hist_frames=None):
+                 device="cuda", with_scores: bool = True, hist_frames=None, token_cfg=None):
         import torch
-        if hist_frames is None:
+        if token_cfg is not None:
+            self.kept_tokens, self.workspace_bytes = fkv_plan_tokens(desc, token_cfg, head_role)
+        elif hist_frames is None:
             self.kept_tokens, self.workspace_bytes = fkv_plan(desc, head_role, static_keep_mask,
                                                               budget_m)
         else:
@@ -230,6 +243,28 @@ def fkv_refresh_current(desc: FkvDesc, cur_k, cur_v, ckv: CompressedKV, stream=N
     lib = load()
     s = ckv.struct()
     _check(lib.fkv_refresh_current(ctypes.byref(desc), _ptr(cur_k), _ptr(cur_v), ctypes.byref(s),
+                                   _stream(stream)))
+
+
+def fkv_plan_tokens(desc: FkvDesc, cfg: FkvTokenCfg, head_role):
+    """Returns (kept_tokens, workspace_bytes) of the token-granular variant."""
+    lib = load()
+    role = _host_u8(head_role)
+    kept = ctypes.c_int64(0)
+    ws = ctypes.c_size_t(0)
+    _check(lib.fkv_plan_tokens(ctypes.byref(desc), ctypes.byref(cfg), role.ctypes.data,
+                               ctypes.byref(kept), ctypes.byref(ws)))
+    return kept.value, ws.value
+
+
+def fkv_compress_tokens(desc: FkvDesc, cfg: FkvTokenCfg, q, k_cache, v_cache, head_role,
+                        ckv: CompressedKV, row_src=None, stream=None) -> None:
+    lib = load()
+    role = _host_u8(head_role)
+    out = ckv.struct()
+    _check(lib.fkv_compress_tokens(ctypes.byref(desc), ctypes.byref(cfg), _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), role.ctypes.data, ctypes.byref(out),
+                                   _ptr(row_src), _ptr(ckv.workspace), ckv.workspace_bytes,
                                    _stream(stream)))
 
 

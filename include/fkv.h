@@ -167,6 +167,42 @@ fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, cons
 fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
                                   int32_t cur_frames, int32_t cap, uint8_t *mask);
 
+/* ---- Token-granular variant ----------------------------------------------
+ * Static heads keep positions at token granularity ([S] 关键模块 1 and 2:
+ * their attention sits on the start and end tokens of a chunk); dynamic heads
+ * keep single tokens chosen by a participative score (Deep Forcing page,
+ * 3.1: sink, recent and candidate zones, top-C candidates by the summed
+ * query-key products of the recent queries).  History token t of a head is
+ * window row t (frames oldest first); the plain-window layout of fkv_compress. */
+typedef struct fkv_token_cfg {
+  int32_t sink_frames;      /* leading history frames kept whole (every head)      */
+  int32_t recent_frames;    /* trailing history frames kept whole (dynamic heads)  */
+  int32_t budget_tokens;    /* C: candidate tokens a dynamic head keeps by score   */
+  int32_t boundary_tokens;  /* L: tokens kept at each end of every history chunk
+                               of cur_frames frames (static heads)                */
+} fkv_token_cfg_t;
+
+/* Kept rows and workspace bytes of fkv_compress_tokens (host only).  Static
+ * head: its sink tokens plus the first and last L tokens of every aligned
+ * history chunk (a trailing partial chunk included); dynamic head: sink and
+ * recent frames plus min(C, candidates); every head then the current chunk. */
+fkv_status_t fkv_plan_tokens(const fkv_desc_t *desc, const fkv_token_cfg_t *cfg,
+                             const uint8_t *head_role, int64_t *kept_tokens,
+                             size_t *workspace_bytes);
+
+/* Token-granular compression of one layer.  Dynamic head h: candidate token j
+ * (between the sink and recent zones) scores phi_j = sum_r q_r . k_j over the
+ * sampled queries r = 0, s, 2s, ... of the current chunk; the C highest are
+ * kept, ties to the lower token index.  Writes out->k, out->v (rows: kept
+ * history tokens ascending, then the current chunk) and out->tok_off; row_src
+ * (device [kept_tokens], may be NULL) receives the window token index of
+ * every compacted row.  q, k_cache, v_cache, workspace as for fkv_compress. */
+fkv_status_t fkv_compress_tokens(const fkv_desc_t *desc, const fkv_token_cfg_t *cfg,
+                                 const void *q, const void *k_cache, const void *v_cache,
+                                 const uint8_t *head_role, const fkv_ckv_t *out,
+                                 int32_t *row_src, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* ---- Offline head profiling ([S] 关键模块 1) --------------------------------
  * Run on a few warm-up samples before inference; produces the head labels and
  * static keep masks that fkv_plan / fkv_compress take. */

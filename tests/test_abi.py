@@ -289,3 +289,44 @@ def test_compress_ragged_and_refresh_argument_errors(lib):
                                    None) == fkv.FKV_ERR_NULL
     assert lib.fkv_refresh_current(ctypes.byref(d), None, 0x200, ctypes.byref(hist),
                                    None) == fkv.FKV_ERR_NULL
+
+
+# ---- token-granular variant: host plan --------------------------------------
+
+def test_plan_tokens_matches_oracle(lib):
+    """Kept rows of the token-granular plan against the oracle's compaction on
+    random configurations (zones overlapping, budgets beyond the candidates,
+    partial trailing chunks, end tokens covering whole chunks)."""
+    rng = np.random.default_rng(7)
+    for trial in range(80):
+        H, T, Fh, Fc = int(rng.integers(1, 6)), int(rng.integers(1, 9)), \
+            int(rng.integers(0, 11)), int(rng.integers(1, 5))
+        cfg = fkv.FkvTokenCfg(int(rng.integers(0, 4)), int(rng.integers(0, 5)),
+                              int(rng.integers(0, 60)), int(rng.integers(0, 2 * T * Fc + 2)))
+        role = rng.integers(0, 2, H).astype(np.uint8)
+        d = fkv.make_desc(H, 128, T, Fh, Fc, 2)
+        kept, ws = fkv.fkv_plan_tokens(d, cfg, role)
+        D = 4
+        n_win = (Fh + Fc) * T
+        z = np.zeros((n_win, H, D), dtype=np.float32)
+        r = O.compress_tokens(z[:Fc * T], z, z, role, T, Fh, Fc, 2, cfg.sink_frames,
+                              cfg.recent_frames, cfg.budget_tokens, cfg.boundary_tokens)
+        assert kept == int(r["tok_off"][-1]), (trial, H, T, Fh, Fc, list(role))
+
+
+def test_plan_tokens_errors(lib):
+    d = fkv.make_desc(2, 128, 8, 6, 3, 2)
+    role = np.array([0, 1], dtype=np.uint8)
+    with pytest.raises(fkv.FkvError):
+        fkv.fkv_plan_tokens(d, fkv.FkvTokenCfg(-1, 0, 4, 2), role)
+    with pytest.raises(fkv.FkvError) as e:
+        fkv.fkv_plan_tokens(d, fkv.FkvTokenCfg(1, 1, -4, 2), role)
+    assert e.value.status == fkv.FKV_ERR_BUDGET
+    kept = ctypes.c_int64(0)
+    assert lib.fkv_plan_tokens(ctypes.byref(d), None, role.ctypes.data, ctypes.byref(kept),
+                               None) == fkv.FKV_ERR_NULL
+    cfg = fkv.FkvTokenCfg(1, 1, 4, 2)
+    out = fkv.FkvCkv(0x1000, 0x2000, 0x3000, None, None, None, 1)   # too small
+    assert lib.fkv_compress_tokens(ctypes.byref(d), ctypes.byref(cfg), 0x10, 0x20, 0x30,
+                                   role.ctypes.data, ctypes.byref(out), None, 0x40, 1 << 20,
+                                   None) == fkv.FKV_ERR_CAPACITY
