@@ -199,6 +199,35 @@ def measure_rolling(wname, args, fkv, torch, W, n_chunks=8):
     }
 
 
+def measure_tokens(wname, args, fkv, torch, W):
+    """Token-granular variant on one layer: sink frame, the last chunk as the
+    recent zone, nine frames' worth of candidate tokens per dynamic head, half
+    a frame at each chunk end for static heads.  Times fkv_compress_tokens
+    and a step (compress + attend)."""
+    w = W.WORKLOADS[wname]
+    T = w.tokens_per_frame
+    inp = W.generate_layer(w, 0)
+    L = Layer(w, inp, fkv, torch)
+    cfg = fkv.FkvTokenCfg(1, w.cur_frames, 9 * T, T // 2)
+    ckv = fkv.CompressedKV(L.desc, inp.head_role, None, 0, token_cfg=cfg)
+
+    def compress(_):
+        fkv.fkv_compress_tokens(L.desc, cfg, L.q, L.k, L.v, inp.head_role, ckv)
+
+    def step(_):
+        compress(None)
+        fkv.fkv_attend(L.desc, L.q, ckv, L.out)
+
+    ms_c = time_loop(compress, [None], args.steps, args.warmup, torch)
+    ms_s = time_loop(step, [None], args.steps, args.warmup, torch)
+    return {"workload": w.name,
+            "config": {"sink_frames": 1, "recent_frames": w.cur_frames,
+                       "budget_tokens": 9 * T, "boundary_tokens": T // 2},
+            "kept_rows": ckv.kept_tokens,
+            "kept_fraction_of_window": ckv.kept_tokens / float(w.n_win * w.num_heads),
+            "ms_compress": ms_c, "ms_per_step": ms_s, "value": w.n_q / (ms_s * 1e-3)}
+
+
 def measure_profile(wname, args, fkv, torch, W, stride=1):
     """Head profiling over every query of one warm-up sample
     (fkv_profile_heads, query stride 1): time per call and the score
@@ -343,6 +372,7 @@ def main():
     if w.dtype == "bf16" and not args.no_rolling and args.layers <= 1:
         line["rolling"] = measure_rolling(w.name, args, fkv, torch, W)
         line["head_profiling"] = measure_profile(w.name, args, fkv, torch, W)
+        line["token_variant"] = measure_tokens(w.name, args, fkv, torch, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:

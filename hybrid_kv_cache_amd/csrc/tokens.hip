@@ -9,15 +9,17 @@
 //
 // Kernels, in launch order:
 //   qsum_kernel    per dynamic head, Qsum[d] = sum over sampled rows of q[r, h, d]
-//                  (fp32, rows in order);
+//                  (fp32, fixed grouping of the rows);
 //   phi_kernel     phi[j] = k_j . Qsum for every candidate token (one thread
 //                  per token, fp32, dims in order) -- sum_r q_r . k_j regrouped;
 //   token_select_kernel
 //                  one workgroup per head: the kept history tokens in
 //                  ascending order (static: pattern flags; dynamic: a 4-pass
 //                  8-bit radix select finds the C-th largest phi, ties to the
-//                  lower index), written as the window token index of every
-//                  compacted row, plus the current chunk;
+//                  lower index; each thread then walks its own run of
+//                  candidates, placed by one scan of the per-thread counts),
+//                  written as the window token index of every compacted row,
+//                  plus the current chunk;
 //   gather_kernel  copies the K and V rows those indices name.
 #include "fkv_device.h"
 #include "fkv_launch.h"
@@ -26,6 +28,7 @@ namespace fkv {
 namespace {
 
 constexpr int kSelThreads = 1024;
+constexpr int kLdsKeys = 24576;   // candidates staged in LDS (96 KiB)
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -34,15 +37,35 @@ __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
 
+// 1024 threads per dynamic head: dim d = tid % D, group g = tid / D takes
+// the sampled rows g, g + G, g + 2G, ... (G = 1024 / D groups, four running
+// sums in flight); the groups' partial sums are then added in group order.
 template <typename T>
-__global__ __launch_bounds__(128) void qsum_kernel(TokenArgs a) {
+__global__ __launch_bounds__(kSelThreads) void qsum_kernel(TokenArgs a) {
+  __shared__ float part[kSelThreads];
   const int di = blockIdx.x, h = a.dyn_heads[di];
-  const int64_t hd = (int64_t)a.H * a.D;
-  const T *q = reinterpret_cast<const T *>(a.q) + (int64_t)h * a.D;
-  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-    float s = 0.f;
-    for (int r = 0; r < a.n_q; r += a.stride) s += to_f32<T>(q[(int64_t)r * hd + d]);
-    a.qsum[di * a.D + d] = s;
+  const int tid = threadIdx.x, D = a.D, G = kSelThreads / D;
+  const int d = tid % D, g = tid / D;
+  const int64_t hd = (int64_t)a.H * D;
+  const int n_s = (a.n_q + a.stride - 1) / a.stride;
+  const T *q = reinterpret_cast<const T *>(a.q) + (int64_t)h * D + d;
+  const int64_t step = (int64_t)G * a.stride * hd;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int j = g;
+  const T *p = q + (int64_t)g * a.stride * hd;
+  for (; j + 3 * G < n_s; j += 4 * G, p += 4 * step) {
+    s0 += to_f32<T>(p[0]);
+    s1 += to_f32<T>(p[step]);
+    s2 += to_f32<T>(p[2 * step]);
+    s3 += to_f32<T>(p[3 * step]);
+  }
+  for (; j < n_s; j += G, p += step) s0 += to_f32<T>(p[0]);
+  part[tid] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (g == 0) {
+    float s = part[d];
+    for (int k = 1; k < G; ++k) s += part[k * D + d];
+    a.qsum[di * D + d] = s;
   }
 }
 
@@ -99,15 +122,58 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
   return before + x - v;
 }
 
-__device__ __forceinline__ bool static_keeps(const TokenArgs &a, int t) {
-  if (t < a.sink_tok) return true;
+// Static pattern over a run of history tokens [lo, hi): calls f(t) for each
+// kept token in order (sink tokens, and the first and last `boundary` tokens
+// of every aligned chunk of F_c frames).  One division per run.
+template <typename F>
+__device__ __forceinline__ void static_run(const TokenArgs &a, int lo, int hi, F f) {
   const int chunk = a.F_c * a.T;
-  const int lo = (t / chunk) * chunk;
-  const int hi = min(lo + chunk, a.n_hist);
-  return t - lo < a.boundary || hi - t <= a.boundary;
+  int c0 = (lo / chunk) * chunk;
+  for (int t = lo; t < hi; ++t) {
+    if (t >= c0 + chunk) c0 += chunk;
+    const int c1 = min(c0 + chunk, a.n_hist);
+    if (t < a.sink_tok || t - c0 < a.boundary || c1 - t <= a.boundary) f(t);
+  }
+}
+
+// Wave 0 finds the digit of the next radix pass: the largest d such that the
+// bins above d hold fewer than `need` keys (bins from 255 down, four per lane).
+__device__ __forceinline__ void pick_digit(const int *hist, uint32_t prefix, int shift, int need,
+                                           uint32_t *s_prefix, int *s_remaining) {
+  const int lane = threadIdx.x & 63;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = hist[255 - 4 * lane - i];
+    sum += c[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  int acc = incl - sum;  // keys in the bins above this lane's four
+  int hit = -1, before = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (hit < 0 && acc + c[i] >= need) {
+      hit = 255 - 4 * lane - i;
+      before = acc;
+    }
+    acc += c[i];
+  }
+  const unsigned long long hits = __ballot(hit >= 0);
+  if (hits != 0 && lane == __ffsll((long long)hits) - 1) {
+    *s_prefix = prefix | ((uint32_t)hit << shift);
+    *s_remaining = need - before;
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) {
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ uint32_t lds_keys[kLdsKeys];
+  __shared__ int whist[kWaves * 256];
   __shared__ int hist[256];
   __shared__ int wsum[kSelThreads / 64];
   __shared__ uint32_t s_prefix;
@@ -122,21 +188,29 @@ __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) 
   int pos = 0;  // rows written so far (uniform)
 
   if (di < 0) {
-    // static pattern over the history, in token order
-    for (int base = 0; base < a.n_hist; base += kSelThreads) {
-      const int t = base + tid;
-      const int keep = t < a.n_hist && static_keeps(a, t);
-      int total;
-      const int p = block_excl_scan(keep, wsum, &total);
-      if (keep) out[pos + p] = t;
-      pos += total;
-    }
+    // static pattern over the history: thread t walks its own run of tokens,
+    // one scan of the per-thread counts places them in token order
+    const int per = (a.n_hist + kSelThreads - 1) / kSelThreads;
+    const int lo = min(tid * per, a.n_hist), hi = min(lo + per, a.n_hist);
+    int cnt = 0;
+    static_run(a, lo, hi, [&](int) { ++cnt; });
+    int total;
+    int p = block_excl_scan(cnt, wsum, &total);
+    static_run(a, lo, hi, [&](int t) { out[p++] = t; });
+    pos = total;
   } else {
     // sink zone
     for (int t = tid; t < a.sink_tok; t += kSelThreads) out[t] = t;
     pos = a.sink_tok;
     const float *phi = a.phi + (int64_t)di * a.n_cand;
     const int n = a.n_cand, c = min(a.budget, n);
+    // The keys are read 6 times; up to kLdsKeys of them are staged in LDS.
+    const bool in_lds = n <= kLdsKeys;
+    if (in_lds) {
+      for (int j = tid; j < n; j += kSelThreads) lds_keys[j] = sort_key(phi[j]);
+      __syncthreads();
+    }
+    auto key_at = [&](int j) -> uint32_t { return in_lds ? lds_keys[j] : sort_key(phi[j]); };
     uint32_t thr = 0;
     int remaining = 0;  // keys equal to thr to take, lowest index first
     if (c > 0 && c < n) {
@@ -145,23 +219,35 @@ __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) 
       int need = c;
       for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        // one histogram per wave (keys of similar size share their top bits,
+        // so a single one would serialise every wave on a few bins)
+        for (int i = tid; i < kWaves * 256; i += kSelThreads) whist[i] = 0;
         __syncthreads();
-        for (int j = tid; j < n; j += kSelThreads) {
-          const uint32_t key = sort_key(phi[j]);
-          const bool match = pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8));
-          if (match) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        int *mine = whist + (tid >> 6) * 256;
+        const uint32_t want = prefix >> (shift + 8);
+        int j = tid;
+        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {
+          uint32_t k4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) k4[u] = key_at(j + u * kSelThreads);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (pass == 0 || (k4[u] >> (shift + 8)) == want)
+              atomicAdd(&mine[(k4[u] >> shift) & 255u], 1);
+        }
+        for (; j < n; j += kSelThreads) {
+          const uint32_t key = key_at(j);
+          if (pass == 0 || (key >> (shift + 8)) == want) atomicAdd(&mine[(key >> shift) & 255u], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-          int acc = 0, d = 255;
-          for (; d > 0; --d) {
-            if (acc + hist[d] >= need) break;
-            acc += hist[d];
-          }
-          s_prefix = prefix | ((uint32_t)d << shift);
-          s_remaining = need - acc;
+        if (tid < 256) {
+          int sum = 0;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) sum += whist[w * 256 + tid];
+          hist[tid] = sum;
         }
+        __syncthreads();
+        if (tid < 64) pick_digit(hist, prefix, shift, need, &s_prefix, &s_remaining);
         __syncthreads();
         prefix = s_prefix;
         need = s_remaining;
@@ -170,30 +256,40 @@ __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) 
       thr = prefix;
       remaining = need;
     }
-    // kept candidates in index order: key > thr, or key == thr among the
-    // first `remaining` such (all of them when c == n, none when c == 0)
-    int eq_seen = 0;
-    for (int base = 0; base < n; base += kSelThreads) {
-      const int j = base + tid;
-      bool gt = false, eq = false;
-      if (j < n && c > 0) {
-        if (c >= n) {
-          gt = true;
-        } else {
-          const uint32_t key = sort_key(phi[j]);
-          gt = key > thr;
-          eq = key == thr;
+    // Kept candidates in index order: key > thr, or key == thr among the
+    // first `remaining` such (all when c == n, none when c == 0).  Thread t
+    // walks its own run; with gt / eq counts before a candidate, its row is
+    // gt_before + min(eq_before, remaining).
+    const int per = (n + kSelThreads - 1) / kSelThreads;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    const bool all = c >= n, none = c == 0;
+    int gt = 0, eq = 0;
+    if (!all && !none) {
+      for (int j = lo; j < hi; ++j) {
+        const uint32_t key = key_at(j);
+        gt += key > thr;
+        eq += key == thr;
+      }
+    }
+    int gt_total, eq_total;
+    int gt_b = block_excl_scan(gt, wsum, &gt_total);
+    int eq_b = block_excl_scan(eq, wsum, &eq_total);
+    if (all) {
+      for (int j = lo; j < hi; ++j) out[pos + j] = a.cand_lo + j;
+    } else if (!none) {
+      for (int j = lo; j < hi; ++j) {
+        const uint32_t key = key_at(j);
+        const int row = gt_b + min(eq_b, remaining);
+        if (key > thr) {
+          out[pos + row] = a.cand_lo + j;
+          ++gt_b;
+        } else if (key == thr) {
+          if (eq_b < remaining) out[pos + row] = a.cand_lo + j;
+          ++eq_b;
         }
       }
-      int eq_total;
-      const int eq_rank = eq_seen + block_excl_scan(eq ? 1 : 0, wsum, &eq_total);
-      eq_seen += eq_total;
-      const int take = gt || (eq && eq_rank < remaining);
-      int total;
-      const int p = block_excl_scan(take, wsum, &total);
-      if (take) out[pos + p] = a.cand_lo + j;
-      pos += total;
     }
+    pos += c;
     // recent zone
     for (int t = tid; t < a.recent_tok; t += kSelThreads) out[pos + t] = a.cand_hi + t;
     pos += a.recent_tok;
@@ -231,9 +327,9 @@ hipError_t launch_tokens(const TokenArgs &a, hipStream_t s) {
   const bool bf16 = a.elt == 2;
   if (a.n_dyn > 0) {
     if (bf16)
-      hipLaunchKernelGGL(qsum_kernel<__bf16>, dim3(a.n_dyn), dim3(128), 0, s, a);
+      hipLaunchKernelGGL(qsum_kernel<__bf16>, dim3(a.n_dyn), dim3(kSelThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(qsum_kernel<float>, dim3(a.n_dyn), dim3(128), 0, s, a);
+      hipLaunchKernelGGL(qsum_kernel<float>, dim3(a.n_dyn), dim3(kSelThreads), 0, s, a);
     if (a.n_cand > 0) {
       dim3 g((a.n_cand + 255) / 256, a.n_dyn);
       if (bf16)
