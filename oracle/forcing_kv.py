@@ -544,6 +544,92 @@ def compress_tokens(q, k, v, head_role, tokens_per_frame: int, hist_frames: int,
                 cand=(cand_lo, cand_hi))
 
 
+# ---- FP8 (OCP e4m3) compressed cache ----------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 e4m3 codes -> exact float64: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the
+    finite maximum is 0x7E = 448 and 0x7F / 0xFF are NaN (the format's
+    definition in the OCP 8-bit floating point specification)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return sign * v
+
+
+def e4m3_encode(x32: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3 codes, round to nearest with ties to even,
+    magnitudes above 448 saturated to 448.  Written from the format: in
+    binade E (value in [2^E, 2^(E+1)), E >= -6; below 2^-6 the subnormal
+    step of the E = -6 binade applies) the representable values are
+    r * 2^(E-3) with r integer, and their codes are (E + 6) * 8 + r, a
+    monotone numbering in which r = 16 rolls over into the next binade."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, e = np.frexp(a)
+    E = np.maximum(e - 1, -6)
+    r = np.round(a / np.ldexp(1.0, E - 3))          # numpy rounds halves to even
+    code = np.where(a == 0, 0, (E + 6) * 8 + r).astype(np.int64)
+    code = np.minimum(code, 0x7E)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3(x, scale: float) -> np.ndarray:
+    """Per-tensor scaled quantization: code of float32(x) / float32(scale)
+    (an IEEE float32 division, then e4m3_encode).  x: float32 values or bf16
+    bit patterns."""
+    xf = decode_bf16(x).astype(np.float32) if np.asarray(x).dtype == np.uint16 \
+        else np.asarray(x, dtype=np.float32)
+    return e4m3_encode(xf / np.float32(scale))
+
+
+def compress_fp8(q, k, v, head_role, static_keep_mask, budget_m: int, tokens_per_frame: int,
+                 hist_frames: int, cur_frames: int, query_stride: int, k_scale, v_scale,
+                 scale: float = 0.0) -> Dict[str, np.ndarray]:
+    """compress() with the compacted rows stored as e4m3 codes: row j of head
+    h holds quantize_e4m3(k_row, k_scale[h]) (and v likewise) -- the pages
+    stack the method with quantization to compress memory further."""
+    r = compress(q, k, v, head_role, static_keep_mask, budget_m, tokens_per_frame, hist_frames,
+                 cur_frames, query_stride, scale)
+    H = len(head_role)
+    k8 = np.empty(r["k_c"].shape, dtype=np.uint8)
+    v8 = np.empty(r["v_c"].shape, dtype=np.uint8)
+    for h in range(H):
+        lo, hi = int(r["tok_off"][h]), int(r["tok_off"][h + 1])
+        k8[lo:hi] = quantize_e4m3(r["k_c"][lo:hi], k_scale[h])
+        v8[lo:hi] = quantize_e4m3(r["v_c"][lo:hi], v_scale[h])
+    r["k8"], r["v8"] = k8, v8
+    return r
+
+
+def attend_fp8(q, k8, v8, tok_off, q_scale, k_scale, v_scale, scale: float = 0.0,
+               rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Attention with e4m3 operands: the queries are quantized per head
+    (quantize_e4m3(q, q_scale[h])), keys and values are the cache's codes;
+    everything is then decoded exactly and attention runs in float64 on
+    q_hat * q_scale, k_hat * k_scale, v_hat * v_scale.  (Rounding the softmax
+    weights for an fp8 value product is the kernel's own approximation and
+    is not modelled here.)"""
+    H = q.shape[1]
+    qf = np.empty(q.shape, dtype=np.float64)
+    for h in range(H):
+        qf[:, h] = e4m3_decode(quantize_e4m3(q[:, h], q_scale[h])) * np.float64(q_scale[h])
+    kf = np.empty(k8.shape, dtype=np.float64)
+    vf = np.empty(v8.shape, dtype=np.float64)
+    for h in range(H):
+        lo, hi = int(tok_off[h]), int(tok_off[h + 1])
+        kf[lo:hi] = e4m3_decode(k8[lo:hi]) * np.float64(k_scale[h])
+        vf[lo:hi] = e4m3_decode(v8[lo:hi]) * np.float64(v_scale[h])
+    return attend(qf, kf, vf, tok_off, scale, rows)
+
+
 def cutoff_band(score_row: np.ndarray, budget_m: int, rel: float = TIE_REL):
     """Frames whose membership in the top-m set is decided by a near tie.
 
