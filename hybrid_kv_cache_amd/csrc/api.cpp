@@ -17,6 +17,7 @@
 
 #include "fkv.h"
 #include "fkv_launch.h"
+#include "fkv_fp8.h"
 
 namespace {
 
@@ -217,9 +218,11 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
 
 // Scoring, selection and compaction of one layer over the window `win`
 // (plain or rolling) with the plan p.
+// kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
 fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
                              const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             size_t workspace_bytes, void *stream,
+                             const float *kv_scales = nullptr) {
   if (!q) return fail(FKV_ERR_NULL, "q is NULL");
   if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
   if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
@@ -284,7 +287,23 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
   }
   // 3. compaction
-  {
+  if (kv_scales) {
+    fkv::CompactFp8Args ca;
+    ca.slots = slots;
+    ca.win = win;
+    ca.k_out = reinterpret_cast<uint8_t *>(out->k);
+    ca.v_out = reinterpret_cast<uint8_t *>(out->v);
+    ca.T = p.T;
+    ca.chunks = (p.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
+    ca.D = p.D;
+    std::memcpy(ca.fh, p.fh, sizeof(ca.fh));
+    for (int h = 0; h < fkv::kMaxHeads; ++h) {
+      ca.k_scale[h] = h < p.H ? kv_scales[h] : 1.f;
+      ca.v_scale[h] = h < p.H ? kv_scales[p.H + h] : 1.f;
+    }
+    hipError_t e = fkv::launch_compact_fp8(ca, p.slot_off[p.H], s);
+    if (e != hipSuccess) return hip_fail(e, "quantizing compaction kernel launch");
+  } else {
     fkv::CompactArgs ca;
     ca.slots = slots;
     ca.win = win;
@@ -409,6 +428,62 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
                          workspace_bytes, stream);
+}
+
+namespace {
+fkv_status_t check_scales(const fkv_desc_t *d, const float *sc, int n, const char *what) {
+  if (d->dtype != FKV_BF16) return fail(FKV_ERR_DTYPE, "the fp8 cache needs bf16 inputs");
+  if (!sc) return fail(FKV_ERR_NULL, "%s is NULL", what);
+  for (int i = 0; i < n; ++i)
+    if (!(sc[i] > 0.f) || !std::isfinite(sc[i]))
+      return fail(FKV_ERR_SHAPE, "%s[%d] = %g is not a positive finite scale", what, i,
+                  (double)sc[i]);
+  return FKV_OK;
+}
+}  // namespace
+
+fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                              const void *v_cache, const uint8_t *head_role,
+                              const uint8_t *static_keep_mask, int32_t budget_m,
+                              const float *kv_scales, const fkv_ckv_t *out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  st = check_scales(desc, kv_scales, 2 * desc->num_heads, "kv_scales");
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
+                         workspace_bytes, stream, kv_scales);
+}
+
+fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
+                            const float *scales, void *out, void *stream) {
+  fkv_status_t st = check_desc(desc);
+  if (st != FKV_OK) return st;
+  st = check_scales(desc, scales, 3 * desc->num_heads, "scales");
+  if (st != FKV_OK) return st;
+  if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");
+  if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
+    return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  fkv::AttendFp8Args a;
+  a.q = q;
+  a.k = reinterpret_cast<const uint8_t *>(ckv->k);
+  a.v = reinterpret_cast<const uint8_t *>(ckv->v);
+  a.out = out;
+  a.tok_off = ckv->tok_off;
+  a.n_q = desc->cur_frames * desc->tokens_per_frame;
+  a.H = desc->num_heads;
+  a.c = log2e_scale(*desc);
+  const int H = desc->num_heads;
+  for (int h = 0; h < fkv::kMaxHeads; ++h) {
+    a.q_scale[h] = h < H ? scales[h] : 1.f;
+    a.k_scale[h] = h < H ? scales[H + h] : 1.f;
+    a.v_scale[h] = h < H ? scales[2 * H + h] : 1.f;
+  }
+  hipError_t e = fkv::launch_attend_fp8(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 attention kernel launch");
+  return ok();
 }
 
 fkv_status_t fkv_plan_ragged(const fkv_desc_t *desc, const int32_t *hist_frames,

@@ -26,7 +26,8 @@ FKV_STATIC, FKV_DYNAMIC = 0, 1
 
 EXPORTED = ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
             "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
-            "fkv_compress_tokens", "fkv_profile_workspace",
+            "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
+            "fkv_profile_workspace",
             "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
             "fkv_attend", "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
 
@@ -82,6 +83,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(I64), ctypes.POINTER(SZ)]
     lib.fkv_compress_tokens.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(FkvTokenCfg), P,
                                         P, P, P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
+    lib.fkv_compress_fp8.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32, P,
+                                     ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_attend_fp8.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, P]
     lib.fkv_profile_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_profile_heads.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, SZ, P]
     lib.fkv_classify_heads.argtypes = [ctypes.POINTER(FkvDesc), P, I32, ctypes.c_float, P, P, P]
@@ -90,7 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
     for name in ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
                  "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
-            "fkv_compress_tokens", "fkv_profile_workspace",
+                 "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
+                 "fkv_profile_workspace",
                  "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
                  "fkv_attend", "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
@@ -182,7 +187,8 @@ class CompressedKV:
     With hist_frames (per-head history lengths), sized for fkv_compress_ragged."""
 
     def __init__(self, desc: FkvDesc, head_role, static_keep_mask, budget_m: int,
-                 device="cuda", with_scores: bool = True, hist_frames=None, token_cfg=None):
+                 device="cuda", with_scores: bool = True, hist_frames=None, token_cfg=None,
+                 fp8: bool = False):
         import torch
         if token_cfg is not None:
             self.kept_tokens, self.workspace_bytes = fkv_plan_tokens(desc, token_cfg, head_role)
@@ -194,6 +200,8 @@ class CompressedKV:
                 desc, hist_frames, head_role, static_keep_mask, budget_m)
         H, D, Fh = desc.num_heads, desc.head_dim, desc.hist_frames
         dt = torch.bfloat16 if desc.dtype == FKV_BF16 else torch.float32
+        if fp8:
+            dt = torch.uint8      # e4m3 codes
         self.k = torch.empty((max(self.kept_tokens, 1), D), dtype=dt, device=device)
         self.v = torch.empty((max(self.kept_tokens, 1), D), dtype=dt, device=device)
         self.tok_off = torch.empty(H + 1, dtype=torch.int64, device=device)
@@ -266,6 +274,33 @@ def fkv_compress_tokens(desc: FkvDesc, cfg: FkvTokenCfg, q, k_cache, v_cache, he
                                    _ptr(v_cache), role.ctypes.data, ctypes.byref(out),
                                    _ptr(row_src), _ptr(ckv.workspace), ckv.workspace_bytes,
                                    _stream(stream)))
+
+
+def _host_f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def fkv_compress_fp8(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask,
+                     budget_m: int, k_scale, v_scale, ckv: CompressedKV, stream=None) -> None:
+    """fkv_compress writing an e4m3 cache (ckv allocated with fp8=True)."""
+    lib = load()
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    sc = _host_f32(np.concatenate([np.ravel(k_scale), np.ravel(v_scale)]))
+    out = ckv.struct()
+    _check(lib.fkv_compress_fp8(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                role.ctypes.data, mask.ctypes.data if mask.size else None,
+                                int(budget_m), sc.ctypes.data, ctypes.byref(out),
+                                _ptr(ckv.workspace), ckv.workspace_bytes, _stream(stream)))
+
+
+def fkv_attend_fp8(desc: FkvDesc, q, ckv: CompressedKV, q_scale, k_scale, v_scale, out,
+                   stream=None) -> None:
+    lib = load()
+    sc = _host_f32(np.concatenate([np.ravel(q_scale), np.ravel(k_scale), np.ravel(v_scale)]))
+    s = ckv.struct()
+    _check(lib.fkv_attend_fp8(ctypes.byref(desc), _ptr(q), ctypes.byref(s), sc.ctypes.data,
+                              _ptr(out), _stream(stream)))
 
 
 def fkv_profile_workspace(desc: FkvDesc) -> int:

@@ -167,6 +167,31 @@ fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, cons
 fkv_status_t fkv_roll_static_mask(int32_t n_frames, const int32_t *frame_ids,
                                   int32_t cur_frames, int32_t cap, uint8_t *mask);
 
+/* ---- FP8 compressed cache ([S] 行业影响 › 与现有产品/工作流的接口: the method
+ * stacks with quantization) --------------------------------------------------
+ * The cache rows are OCP FP8 e4m3 codes (1 byte per element, finite range
+ * +-448, NaN 0x7F/0xFF): element x of head h is stored as the code of
+ * x / scale[h] (an IEEE fp32 division, clamped to +-448, rounded to nearest
+ * even).  Needs bf16 inputs with D = 128; ckv->k and ckv->v hold cap_tokens
+ * rows of D bytes. */
+
+/* As fkv_compress, writing an e4m3 cache.  kv_scales: host [2 H], the K
+ * scales of heads 0 .. H-1, then the V scales (positive, finite). */
+fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                              const void *v_cache, const uint8_t *head_role,
+                              const uint8_t *static_keep_mask, int32_t budget_m,
+                              const float *kv_scales, const fkv_ckv_t *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Attention over an e4m3 cache on the fp8 matrix cores: the bf16 queries of
+ * head h are quantized with scale[h] the same way, scores are
+ * scale * (q_hat . k_hat) * q_scale * k_scale, outputs sum_j p_j v_hat_j *
+ * v_scale / sum_j p_j with the weights p_j themselves rounded to e4m3 for
+ * the value product (the sums use the same rounded weights).  scales: host
+ * [3 H]: Q, K, V scales per head.  out as for fkv_attend (bf16). */
+fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
+                            const float *scales, void *out, void *stream);
+
 /* ---- Token-granular variant ----------------------------------------------
  * Static heads keep positions at token granularity ([S] 关键模块 1 and 2:
  * their attention sits on the start and end tokens of a chunk); dynamic heads

@@ -30,7 +30,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fkv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fkv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
