@@ -26,6 +26,7 @@ import numpy as np
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 METRIC = "compressed-attn query tok/s per layer @480P/1080P; % MFMA & HBM roofline"
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
@@ -228,6 +229,45 @@ def measure_tokens(wname, args, fkv, torch, W):
             "ms_compress": ms_c, "ms_per_step": ms_s, "value": w.n_q / (ms_s * 1e-3)}
 
 
+def measure_fp8(wname, args, fkv, torch, W):
+    """The e4m3 compressed cache on one layer: fkv_compress_fp8 +
+    fkv_attend_fp8 per step (per-head scales amax / 448 of q, k, v), the
+    attention's rate against the dense fp8 MFMA peak, cache bytes."""
+    w = W.WORKLOADS[wname]
+    inp = W.generate_layer(w, 0)
+    L = Layer(w, inp, fkv, torch)
+    H, D = w.num_heads, w.head_dim
+
+    def scales(a):
+        x = np.abs(W.bf16_bits_to_f32(a)).reshape(-1, H, D).max(axis=(0, 2))
+        return np.maximum(x, 1e-6).astype(np.float32) / np.float32(448.0)
+
+    ks, vs, qs = scales(inp.k), scales(inp.v), scales(inp.q)
+    ckv = fkv.CompressedKV(L.desc, inp.head_role, inp.static_keep_mask, w.budget_m, fp8=True)
+
+    def compress(_):
+        fkv.fkv_compress_fp8(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, ks, vs, ckv)
+
+    def attend(_):
+        fkv.fkv_attend_fp8(L.desc, L.q, ckv, qs, ks, vs, L.out)
+
+    def step(_):
+        compress(None)
+        attend(None)
+
+    steps = args.steps if w.tokens_per_frame < 5000 else max(args.steps // 4, 3)
+    ms_s = time_loop(step, [None], steps, args.warmup, torch)
+    ms_c = time_loop(compress, [None], steps, args.warmup, torch)
+    ms_a = time_loop(attend, [None], steps, args.warmup, torch)
+    flop = 4.0 * w.n_q * D * ckv.kept_tokens
+    tf = flop / (ms_a * 1e-3) / 1e12
+    return {"workload": w.name, "ms_per_step": ms_s, "value": w.n_q / (ms_s * 1e-3),
+            "ms_compress": ms_c, "ms_attend": ms_a, "attend_tflops": tf,
+            "attend_frac_of_fp8_peak": tf / FP8_PEAK_TFLOPS,
+            "cache_bytes": 2.0 * ckv.kept_tokens * D,
+            "cache_bytes_bf16": 4.0 * ckv.kept_tokens * D}
+
+
 def measure_profile(wname, args, fkv, torch, W, stride=1):
     """Head profiling over every query of one warm-up sample
     (fkv_profile_heads, query stride 1): time per call and the score
@@ -373,6 +413,8 @@ def main():
         line["rolling"] = measure_rolling(w.name, args, fkv, torch, W)
         line["head_profiling"] = measure_profile(w.name, args, fkv, torch, W)
         line["token_variant"] = measure_tokens(w.name, args, fkv, torch, W)
+        line["fp8_cache"] = [measure_fp8(n, args, fkv, torch, W)
+                             for n in (w.name, args.secondary) if n]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:
