@@ -63,25 +63,20 @@ __device__ __forceinline__ int head_tiles(const AttendArgs &a, int h) {
   return (int)((len + kKT - 1) / kKT);
 }
 
-// Split schedule on XCD x (nb workgroups, nb % 16 == 0, pairs < nb): the
-// XCD's pairs are [p_lo, p_lo + np) and its workgroups xs = 0 .. nb/8 - 1,
-// placed one per CU (xs < nb/16) before any CU takes a second one.  Of two
-// workgroups sharing a CU the older one issues first and runs faster, so
-// when np > nb/16 the first nb/16 workgroups take the first w0 = nb/16
-// pairs whole, and the rest share the remaining R = np - w0 pairs: R main
-// workgroups run tiles [0, split) of one pair each, the ne others the tails
-// [split, tiles) of up to k = ceil(R / ne) pairs each (k = 0: no cut).
+// Split schedule on XCD x (nb workgroups, nb % 8 == 0, at most nb / 2
+// pairs): the XCD's pairs are [p_lo, p_lo + np) and its workgroups
+// xs = 0 .. nb/8 - 1.  The first np workgroups run tiles [0, split) of one
+// pair each (main parts), the ne others the tails [split, tiles) of up to
+// k = ceil(np / ne) pairs each (k = 0: no cut).
 struct XcdSplit {
-  int p_lo, np, w0, ne, k;
+  int p_lo, np, ne, k;
 };
 __device__ __forceinline__ XcdSplit xcd_split(int pairs, int nb, int x) {
   XcdSplit s;
   s.p_lo = pairs * x / 8;
   s.np = pairs * (x + 1) / 8 - s.p_lo;
-  s.w0 = s.np > nb / 16 ? nb / 16 : 0;
-  const int r = s.np - s.w0;
-  s.ne = nb / 8 - s.w0 - r;
-  s.k = s.ne > 0 ? (r + s.ne - 1) / s.ne : 0;
+  s.ne = nb / 8 - s.np;
+  s.k = s.ne > 0 ? (s.np + s.ne - 1) / s.ne : 0;
   return s;
 }
 // First tail tile of a pair with nt tiles (nt when nothing is cut).  A
@@ -125,19 +120,14 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     n_items = 1;
   } else {
     const XcdSplit sp = xcd_split(pairs, nb, x);
-    const int r = sp.np - sp.w0;
-    if (xs < sp.w0) {
+    k = sp.k;
+    if (xs < sp.np) {
       p0 = sp.p_lo + xs;
       n_items = 1;
-    } else if (xs < sp.w0 + r) {
-      p0 = sp.p_lo + xs;
-      n_items = 1;
-      k = sp.k;
     } else {
-      const int e = xs - sp.w0 - r;
-      p0 = sp.p_lo + sp.w0 + e * r / sp.ne;
-      n_items = sp.p_lo + sp.w0 + (e + 1) * r / sp.ne - p0;
-      k = sp.k;
+      const int e = xs - sp.np;
+      p0 = sp.p_lo + e * sp.np / sp.ne;
+      n_items = sp.p_lo + (e + 1) * sp.np / sp.ne - p0;
       tail = 1;
     }
   }
@@ -288,6 +278,10 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     // Next tile's scores (independent of this tile's softmax).  On the last
     // step this reads a stale buffer and the result is never used; it stays
     // unconditional so that the MFMAs can interleave with the softmax.
+    // Issue priority 1 while this wave feeds the score MFMAs and the softmax,
+    // back to 0 for the value product: the two waves sharing a SIMD take
+    // turns instead of the older one running ahead.
+    __builtin_amdgcn_s_setprio(1);
     qk(k_read, sn);
     weights();
     // K-fragment reads run four ahead of the 16 score MFMAs of the next
@@ -304,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (__any(!(lt <= 0x1p64f))) {
       const float mnew = fmaxf(m, tile_max());
       const float alpha = fast_exp2(m - mnew);
@@ -408,7 +403,6 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   int x = 0;
   while (x < 7 && p >= pairs * (x + 1) / 8) ++x;
   const XcdSplit sp = xcd_split(pairs, a.n_wg, x);
-  if (p - sp.p_lo < sp.w0) return;  // written whole
   const int h = p / ntq, qt = p - h * ntq;
   const int nt = head_tiles(a, h);
   const int ts = split_tile(nt, sp.k);
@@ -537,7 +531,7 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
   const int nb = 2 * device_cus();
   a.part = nullptr;
   a.n_wg = pairs;
-  if (part && nb > 0 && nb % 16 == 0 && pairs < nb &&
+  if (part && nb > 0 && nb % 8 == 0 && 2 * pairs <= nb &&
       part_bytes >= (size_t)2 * nb * kPartFloats * sizeof(float)) {
     a.part = static_cast<float *>(part);
     a.n_wg = nb;

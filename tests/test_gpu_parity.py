@@ -177,13 +177,13 @@ def test_late_frames_with_much_larger_scores():
     (100, 1, 3, 1, 36),    # one pair of 7 tiles: cut in halves
     (300, 1, 40, 2, 32),   # 5 pairs x 197 tiles, one tail workgroup per pair
     (257, 7, 9, 3, 33),    # 49 pairs x 49 tiles
-    (1560, 12, 18, 3, 34), # 480P window: 444 pairs x 512 tiles, up to 7 tails each
+    (1560, 12, 18, 3, 34), # 480P window, 444 pairs: per pair even with a workspace
 ])
 def test_split_schedule(T, H, Fh, Fc, seed):
-    """With a workspace and fewer (head, query tile) pairs than resident
-    workgroups, attention cuts pairs into a main part and a tail run by
-    different workgroups and merges the two partial results: the result
-    matches the oracle and the one-workgroup-per-pair schedule."""
+    """With a workspace and at most one (head, query tile) pair per CU,
+    attention cuts pairs into a main part and a tail run by different
+    workgroups and merges the two partial results: the result matches the
+    oracle and the one-workgroup-per-pair schedule."""
     w = W.small_workload(tokens_per_frame=T, num_heads=H, hist_frames=Fh, cur_frames=Fc,
                          budget_m=min(3, Fh), num_static=0, query_stride=7, seed=seed)
     inp = W.generate_layer(w)
