@@ -224,6 +224,9 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       lsum *= alpha;
     }
+    // Issue priority 1 for the score MFMAs and the softmax, 0 for the value
+    // product (the waves sharing a SIMD take turns).
+    __builtin_amdgcn_s_setprio(1);
     qk(k_read, sn);
     // Weights as e4m3 codes: byte i of the B operand = key 32 g + i.
     i32x8 pf;
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
         int v = cvt2<false>(p0, p1, 0);
         pf[4 * kb + t] = cvt2<true>(p2, p3, v);
       }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       i32x8 vf;
