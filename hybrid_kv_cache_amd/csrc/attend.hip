@@ -439,16 +439,20 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   }
 }
 
-// fp32 path (small shapes): one thread per query, keys staged 32 at a time in
-// LDS and read by broadcast; exact online softmax per key.
+// fp32 path (small shapes): a workgroup of 4 waves takes 64 queries of one
+// head, one query per lane; wave w walks the keys w, w + 4, w + 8, ... of
+// each 32-key tile staged in LDS (exact online softmax per key), and the four
+// partial states (m, l, o) are merged in wave order at the end.
 template <int D>
-__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
-  constexpr int KT = 32;
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
+  constexpr int KT = 32, W = 4;
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
-  const int tid = threadIdx.x;
+  __shared__ float part_o[W - 1][64][D + 1];
+  __shared__ float part_ml[W - 1][64][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
-  const int qi = blockIdx.x * 64 + tid;
+  const int qi = blockIdx.x * 64 + lane;
   const float *kb, *vb;
   int64_t rs;
   int len;
@@ -474,13 +478,13 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
   float m = kNegBig, l = 0.f;
   for (int t0 = 0; t0 < len; t0 += KT) {
     const int n = min(KT, len - t0);
-    for (int idx = tid; idx < KT * D; idx += 64) {
+    for (int idx = tid; idx < KT * D; idx += 256) {
       const int j = idx / D, d = idx % D;
       ks[j][d] = j < n ? kb[(t0 + j) * rs + d] : 0.f;
       vs[j][d] = j < n ? vb[(t0 + j) * rs + d] : 0.f;
     }
     __syncthreads();
-    for (int j = 0; j < n; ++j) {
+    for (int j = wave; j < n; j += W) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[j][d], s);
@@ -495,7 +499,23 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
     }
     __syncthreads();
   }
-  if (qi < a.n_q) {
+  if (wave > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) part_o[wave - 1][lane][d] = o[d];
+    part_ml[wave - 1][lane][0] = m;
+    part_ml[wave - 1][lane][1] = l;
+  }
+  __syncthreads();
+  if (wave == 0 && qi < a.n_q) {
+    for (int w = 0; w < W - 1; ++w) {
+      const float m2 = part_ml[w][lane][0], l2 = part_ml[w][lane][1];
+      const float mn = fmaxf(m, m2);
+      const float f1 = fast_exp2(m - mn), f2 = fast_exp2(m2 - mn);
+      l = l * f1 + l2 * f2;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = o[d] * f1 + part_o[w][lane][d] * f2;
+      m = mn;
+    }
     float *op = reinterpret_cast<float *>(a.out) + ((int64_t)qi * a.H + h) * D;
     const float inv = 1.f / l;
 #pragma unroll
@@ -544,9 +564,9 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s) {
   dim3 grid((a.n_q + 63) / 64, a.H);
   if (a.D == 64)
-    hipLaunchKernelGGL(attend_f32_kernel<64>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL(attend_f32_kernel<64>, grid, dim3(256), 0, s, a);
   else if (a.D == 128)
-    hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
