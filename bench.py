@@ -12,6 +12,12 @@ To keep the 256 MB last-level cache from holding a 480P layer's whole window
 between steps, the timed loop walks over several device copies of the layer
 (--copies), so K/V come from HBM as they would in a multi-layer pass.
 
+Also reported (same workload): the rolling compressed cache at its settled
+size ("rolling"), head profiling over every query of a sample
+("head_profiling"), the token-granular variant ("token_variant"), the e4m3
+cache with fp8 attention ("fp8_cache", 480P and 1080P), and the CPU oracle
+on the host ("cpu_baseline").
+
 Prints one JSON line.
 """
 from __future__ import annotations

@@ -64,8 +64,8 @@ __device__ __forceinline__ float pair_sum(float v) {
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier for code that moves data into LDS only through
-// global_load_lds (whose completion the caller waits for explicitly with
-// s_waitcnt vmcnt): waits for this wave's own LDS reads and writes
+// buffer loads with the LDS destination (whose completion the caller waits
+// for explicitly with s_waitcnt vmcnt): waits for this wave's own LDS reads and writes
 // (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it carries no
 // memory fence, so copies still in flight for later tiles are not waited
 // for.  The empty asm statements keep the compiler from moving memory
@@ -121,15 +121,6 @@ __device__ __forceinline__ void buffer_load_lds16x4(buf_rsrc rsrc, const uint32_
   buffer_load_lds16<3072>(rsrc, voff[3], soffset, lds_wave_base);
 }
 
-// 16-byte global -> LDS copy without a register round trip
-// (global_load_lds_dwordx4).  The wave's 64 lanes fill the 1 KiB of LDS at
-// lds_wave_base (wave-uniform) in lane order, 16 bytes per lane.
-__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0,
-                                   0);
-}
-
 __device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_convertvector(v, bf16x2);
@@ -173,23 +164,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char *base, uint32_t off) {
 __device__ __forceinline__ u32x4 lds_read_b128(const char *base, uint32_t off) {
   return *reinterpret_cast<const u32x4 *>(base + off);
 }
-__device__ __forceinline__ u32x2 lds_read_b64(const char *base, uint32_t off) {
-  return *reinterpret_cast<const u32x2 *>(base + off);
-}
 
 // Global 16-byte load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
-
-// Pair two 16-bit halves into one dword: (lo16(a), lo16(b)) or (hi16(a), hi16(b)).
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
 
 // First byte of the T-row frame f of head h's window (fh_h history frames,
 // then the current chunk; see WinView), and the bytes between its rows.
