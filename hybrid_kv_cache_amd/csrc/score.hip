@@ -14,7 +14,10 @@
 // bf16 kernel: workgroup = 4 waves x 32 sampled queries, one frame of one
 // dynamic head; K rows of the frame are copied straight into a four-slot LDS
 // ring in tiles of 64 (three tiles in flight ahead of the one being read);
-// S^T = K Q^T on v_mfma_f32_32x32x16_bf16.
+// S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  Frames are located through the
+// window view: a plain token-major window, or a head's ragged history (a
+// previous compressed cache) followed by the current chunk.  Head profiling
+// runs the same kernel over every head with stride 1.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
