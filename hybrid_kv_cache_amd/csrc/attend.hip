@@ -546,8 +546,8 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
   AttendArgs a = a0;
   const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
   // Two workgroups fit on a CU (64 KiB of LDS each).  The split schedule
-  // runs exactly that many, all resident at once, when there are fewer
-  // pairs; with more, whole pairs are dealt out as workgroups finish.
+  // runs exactly that many, all resident at once, when there is at most one
+  // pair per CU; otherwise whole pairs are dealt out as workgroups finish.
   const int nb = 2 * device_cus();
   a.part = nullptr;
   a.n_wg = pairs;
