@@ -219,3 +219,25 @@ def test_attend_workspace_too_small_is_rejected():
     out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="workspace"):
         fkv.fkv_attend_dense(desc, q, k, v, out, small)
+
+
+def test_random_shapes_sweep():
+    """Twenty seeded random configurations (heads, frame sizes across the
+    64-row tiles, history lengths down to none, chunk sizes, strides, budgets
+    below and above F_h, mixed roles, bf16 and fp32): selection, offsets,
+    compacted rows, compressed and full-KV attention against the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(20):
+        dtype = "bf16" if case % 3 else "f32"
+        Fh = int(rng.integers(0, 13))
+        w = W.small_workload(name=f"sweep{case}_{dtype}", dtype=dtype,
+                             head_dim=128 if dtype == "bf16" else 64,
+                             tokens_per_frame=int(rng.integers(1, 150)),
+                             num_heads=int(rng.integers(1, 9)), hist_frames=Fh,
+                             cur_frames=int(rng.integers(1, 5)),
+                             query_stride=int(rng.integers(1, 9)),
+                             budget_m=int(rng.integers(0, Fh + 3)),
+                             num_static=0, seed=3000 + case)
+        w = W.dataclasses.replace(w, num_static=int(rng.integers(0, w.num_heads + 1)))
+        G.announce(f"sweep case {case}: {w}")
+        full_case(w, W.generate_layer(w))
