@@ -68,6 +68,12 @@ fkv_status_t check_desc(const fkv_desc_t *d) {
   const int64_t n_win = (int64_t)(d->hist_frames + d->cur_frames) * d->tokens_per_frame;
   if (n_win >= (int64_t)1 << 31) return fail(FKV_ERR_SHAPE, "window of %lld tokens too long",
                                             (long long)n_win);
+  // The kernels address K / V through buffer descriptors with 32-bit byte
+  // ranges: one window tensor must stay below 4 GiB.
+  const int64_t win_bytes = n_win * d->num_heads * d->head_dim * elt_bytes(d->dtype);
+  if (win_bytes >= (int64_t)1 << 32)
+    return fail(FKV_ERR_SHAPE, "window tensor of %lld bytes: 4 GiB or more is not supported",
+                (long long)win_bytes);
   return FKV_OK;
 }
 

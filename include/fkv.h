@@ -22,7 +22,8 @@
  *   out      [Nq,    H, D]   same dtype as q
  * Element type: bf16 with D = 128, or fp32 with D = 64 or 128.
  * Limits: 1 <= H <= 64, 0 <= F_h <= 64, 1 <= F_c <= 8, 1 <= T, s >= 1,
- *         N_win < 2^31; element offsets are computed in 64 bits.
+ *         N_win < 2^31, each window tensor (N_win * H * D elements) below
+ *         4 GiB; element offsets are computed in 64 bits.
  *
  * Threading and streams: calls are stateless apart from the thread-local
  * error string; every device operation is enqueued on the given stream

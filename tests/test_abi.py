@@ -108,6 +108,7 @@ def test_plan_examples(lib):
     ("tokens_per_frame", 0, fkv.FKV_ERR_SHAPE),
     ("query_stride", 0, fkv.FKV_ERR_SHAPE),
     ("scale", -1.0, fkv.FKV_ERR_SHAPE),
+    ("tokens_per_frame", 1 << 19, fkv.FKV_ERR_SHAPE),   # 4 GiB window tensor
 ])
 def test_plan_rejects_bad_desc(lib, field, value, status):
     d = fkv.make_desc(4, 128, 16, 6, 3, 4)
@@ -116,6 +117,18 @@ def test_plan_rejects_bad_desc(lib, field, value, status):
                      np.ones((max(d.num_heads, 1), max(d.hist_frames, 0)), np.uint8), 2)
     assert st == status
     assert fkv.fkv_last_error()
+
+
+def test_window_size_limit_edge(lib):
+    """4 GiB is the first window-tensor size refused; one token-row less fits."""
+    # 4 heads x 128 dims x 2 bytes = 1 KiB per token row, 9 frames per window
+    rows_4g = (1 << 32) // 1024
+    d = fkv.make_desc(4, 128, rows_4g // 9 + 1, 6, 3, 4)
+    st, _, _ = _plan(d, np.ones(4, np.uint8), np.zeros((4, 6), np.uint8), 2)
+    assert st == fkv.FKV_ERR_SHAPE and "4 GiB" in fkv.fkv_last_error()
+    d = fkv.make_desc(4, 128, (rows_4g - 1) // 9, 6, 3, 4)
+    st, _, _ = _plan(d, np.ones(4, np.uint8), np.zeros((4, 6), np.uint8), 2)
+    assert st == fkv.FKV_OK
 
 
 def test_plan_null_and_budget(lib):
