@@ -134,12 +134,20 @@ def measure(wname, args, fkv, torch, W):
     ms_dense = time_loop(lambda L: fkv.fkv_attend_dense(L.desc, L.q, L.k, L.v, L.dout,
                                                          L.ckv.attend_ws),
                          layers, args.steps, args.warmup, torch)
+    # per-stage times of the compression (HIP events around each kernel)
+    stages = []
+    for i in range(max(args.steps // 4, 5)):
+        L = layers[i % len(layers)]
+        stages.append(fkv.fkv_compress_timed(L.desc, L.q, L.k, L.v, L.role, L.mask,
+                                             w.budget_m, L.ckv))
+    stage_ms = [float(np.median([x[j] for x in stages])) for j in range(3)]
     kept = sum(L.ckv.kept_tokens for L in layers) / len(layers)  # mean over the layers
     D = w.head_dim
     attn_flop = 4.0 * w.n_q * D * kept
     dense_flop = 4.0 * w.n_q * D * w.n_win * w.num_heads
     elt = 2 if w.dtype == "bf16" else 4
     return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_compress=ms_compress,
+                stage_ms=stage_ms,
                 ms_attend=ms_attend, ms_dense=ms_dense, attn_flop=attn_flop,
                 dense_flop=dense_flop, n_layers=len(layers),
                 compact_bytes=4.0 * kept * D * elt,
@@ -293,6 +301,27 @@ def measure_profile(wname, args, fkv, torch, W, stride=1):
             "score_tflops": flop / (ms * 1e-3) / 1e12}
 
 
+def kernel_rates(r):
+    """Per-kernel times and rates of one measured workload: K1 scoring
+    (2 n_s D N_win H_dyn FLOP against the bf16 peak), K2 selection (latency),
+    K3 compaction (algorithmic bytes against HBM), K4 attention."""
+    w = r["w"]
+    s_ms, sel_ms, c_ms = r["stage_ms"]
+    n_dyn = int((r["inp"].head_role == 1).sum())
+    n_s = -(-w.n_q // w.query_stride)
+    k1 = 2.0 * n_s * w.head_dim * w.n_win * n_dyn
+    k1_tf = k1 / (s_ms * 1e-3) / 1e12 if s_ms > 0 else None
+    k3_gbs = r["compact_bytes"] / (c_ms * 1e-3) / 1e9
+    k4_tf = r["attn_flop"] / (r["ms_attend"] * 1e-3) / 1e12
+    return {"score_us": s_ms * 1e3, "score_tflops": k1_tf,
+            "score_frac_of_peak": k1_tf / BF16_PEAK_TFLOPS if k1_tf else None,
+            "select_us": sel_ms * 1e3,
+            "compact_us": c_ms * 1e3, "compact_gbs": k3_gbs,
+            "compact_frac_of_hbm": k3_gbs / HBM_PEAK_GBS,
+            "attend_us": r["ms_attend"] * 1e3, "attend_tflops": k4_tf,
+            "attend_frac_of_peak": k4_tf / BF16_PEAK_TFLOPS}
+
+
 def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
     """The oracle as it stands, timed on this host over the whole layer
     (scoring, selection, compaction and attention of every query row),
@@ -400,6 +429,7 @@ def main():
         "attention_speedup_vs_full_kv": r["ms_dense"] / r["ms_attend"],
         "kept_fraction_of_history_kv": r["kept_frac_hist"],
         "compact_bytes_per_layer": r["compact_bytes"],
+        "kernels": kernel_rates(r) if w.dtype == "bf16" else None,
     }
     if args.secondary:
         r2 = measure(args.secondary, args, fkv, torch, W)
@@ -413,6 +443,7 @@ def main():
             "attend_frac_of_peak": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12 / peak,
             "speedup_vs_full_kv": r2["ms_dense"] / r2["ms_step"],
             "attention_speedup_vs_full_kv": r2["ms_dense"] / r2["ms_attend"],
+            "kernels": kernel_rates(r2) if w2.dtype == "bf16" else None,
         }
         del r2
     if w.dtype == "bf16" and not args.no_rolling and args.layers <= 1:

@@ -228,7 +228,7 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
 fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
                              const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
                              size_t workspace_bytes, void *stream,
-                             const float *kv_scales = nullptr) {
+                             const float *kv_scales = nullptr, hipEvent_t *ev = nullptr) {
   if (!q) return fail(FKV_ERR_NULL, "q is NULL");
   if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
   if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
@@ -246,6 +246,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   fkv::CopySlot *slots = reinterpret_cast<fkv::CopySlot *>(ws + p.ws_slot_off);
   const float c = log2e_scale(*desc);
 
+  if (ev) hipEventRecord(ev[0], s);
   // 1. dynamic-head scoring: per (sampled query, frame) log-sum-exp
   if (p.n_dyn > 0) {
     fkv::ScoreArgs sa;
@@ -267,6 +268,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
                                            : fkv::launch_score_f32(sa, s);
     if (e != hipSuccess) return hip_fail(e, "scoring kernel launch");
   }
+  if (ev) hipEventRecord(ev[1], s);
   // 2. selection, offsets and compaction slots
   {
     fkv::SelectArgs sa;
@@ -292,6 +294,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     hipError_t e = fkv::launch_select(sa, s);
     if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
   }
+  if (ev) hipEventRecord(ev[2], s);
   // 3. compaction
   if (kv_scales) {
     fkv::CompactFp8Args ca;
@@ -323,6 +326,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     hipError_t e = fkv::launch_compact(ca, p.slot_off[p.H], s);
     if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
   }
+  if (ev) hipEventRecord(ev[3], s);
   return ok();
 }
 
@@ -489,6 +493,35 @@ fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv
   }
   hipError_t e = fkv::launch_attend_fp8(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 attention kernel launch");
+  return ok();
+}
+
+fkv_status_t fkv_compress_timed(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                                const void *v_cache, const uint8_t *head_role,
+                                const uint8_t *static_keep_mask, int32_t budget_m,
+                                const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                                void *stream, float *ms) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  if (!ms) return fail(FKV_ERR_NULL, "ms is NULL");
+  hipEvent_t ev[4] = {};
+  for (int i = 0; i < 4; ++i) {
+    const hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      return hip_fail(e, "event creation");
+    }
+  }
+  st = compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
+                       workspace_bytes, stream, nullptr, ev);
+  hipError_t e = st == FKV_OK ? hipEventSynchronize(ev[3]) : hipSuccess;
+  for (int i = 0; st == FKV_OK && e == hipSuccess && i < 3; ++i)
+    e = hipEventElapsedTime(&ms[i], ev[i], ev[i + 1]);
+  for (int i = 0; i < 4; ++i) hipEventDestroy(ev[i]);
+  if (st != FKV_OK) return st;
+  if (e != hipSuccess) return hip_fail(e, "event timing");
   return ok();
 }
 

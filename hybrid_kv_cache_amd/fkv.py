@@ -24,7 +24,8 @@ FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
 FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
-EXPORTED = ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_timed", "fkv_plan_ragged",
+            "fkv_compress_ragged",
             "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
             "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
             "fkv_profile_workspace",
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(SZ)]
     lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                  ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_compress_timed.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
+                                       ctypes.POINTER(FkvCkv), P, SZ, P, P]
     lib.fkv_plan_ragged.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, I32, ctypes.POINTER(I64),
                                     ctypes.POINTER(SZ)]
     lib.fkv_compress_ragged.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P,
@@ -92,7 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
-    for name in ("fkv_plan", "fkv_compress", "fkv_plan_ragged", "fkv_compress_ragged",
+    for name in ("fkv_plan", "fkv_compress", "fkv_compress_timed", "fkv_plan_ragged",
+                 "fkv_compress_ragged",
                  "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
                  "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
                  "fkv_profile_workspace",
@@ -352,6 +356,22 @@ def _ws(workspace):
     if workspace is None:
         return None, 0
     return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def fkv_compress_timed(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask,
+                       budget_m: int, ckv: CompressedKV, stream=None):
+    """fkv_compress with its stage times: (score_ms, select_ms, compact_ms).
+    Waits for the device."""
+    lib = load()
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    out = ckv.struct()
+    ms = (ctypes.c_float * 3)()
+    _check(lib.fkv_compress_timed(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  role.ctypes.data, mask.ctypes.data if mask.size else None,
+                                  int(budget_m), ctypes.byref(out), _ptr(ckv.workspace),
+                                  ckv.workspace_bytes, _stream(stream), ms))
+    return float(ms[0]), float(ms[1]), float(ms[2])
 
 
 def fkv_attend(desc: FkvDesc, q, ckv: CompressedKV, out, workspace="ckv",

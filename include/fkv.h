@@ -118,6 +118,15 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
                           const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* Measurement helper: fkv_compress with HIP events around its three stages;
+ * waits for the device and writes the stage times in milliseconds to ms[3]
+ * (scoring -- 0 when no head is scored --, selection, compaction). */
+fkv_status_t fkv_compress_timed(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                                const void *v_cache, const uint8_t *head_role,
+                                const uint8_t *static_keep_mask, int32_t budget_m,
+                                const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                                void *stream, float *ms);
+
 /* ---- Rolling compressed cache (a chunk's compressed cache is the next
  * chunk's history) ----------------------------------------------------------
  * [S] 输出与工程收益: the compressed K/V replace the layer's cache.  Kept here

@@ -241,3 +241,25 @@ def test_random_shapes_sweep():
         w = W.dataclasses.replace(w, num_static=int(rng.integers(0, w.num_heads + 1)))
         G.announce(f"sweep case {case}: {w}")
         full_case(w, W.generate_layer(w))
+
+
+def test_compress_timed_matches_compress():
+    """The measurement helper runs the same kernels: identical cache, offsets
+    and selection, and positive stage times (scoring 0 without dynamic heads)."""
+    import torch
+    w = W.small_workload(tokens_per_frame=90, num_heads=4, hist_frames=6, seed=61)
+    inp = W.generate_layer(w)
+    desc, ckv, (q, k, v), _ = G.run_compress(w, inp)
+    ckv2 = fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m)
+    ms = fkv.fkv_compress_timed(desc, q, k, v, inp.head_role, inp.static_keep_mask,
+                                w.budget_m, ckv2)
+    torch.cuda.synchronize()
+    n = ckv.kept_tokens
+    for a, b in ((ckv.k, ckv2.k), (ckv.v, ckv2.v), (ckv.tok_off, ckv2.tok_off),
+                 (ckv.seg_off, ckv2.seg_off), (ckv.seg_idx, ckv2.seg_idx)):
+        assert np.array_equal(fkv.to_host(a)[:n], fkv.to_host(b)[:n])
+    assert all(t > 0 for t in ms), ms
+    role0 = np.zeros(w.num_heads, dtype=np.uint8)
+    ckv3 = fkv.CompressedKV(desc, role0, inp.static_keep_mask, w.budget_m)
+    ms0 = fkv.fkv_compress_timed(desc, q, k, v, role0, inp.static_keep_mask, w.budget_m, ckv3)
+    assert ms0[1] > 0 and ms0[2] > 0 and ms0[0] < ms[0]
