@@ -255,9 +255,11 @@ def test_compress_timed_matches_compress():
                                 w.budget_m, ckv2)
     torch.cuda.synchronize()
     n = ckv.kept_tokens
-    for a, b in ((ckv.k, ckv2.k), (ckv.v, ckv2.v), (ckv.tok_off, ckv2.tok_off),
-                 (ckv.seg_off, ckv2.seg_off), (ckv.seg_idx, ckv2.seg_idx)):
-        assert np.array_equal(fkv.to_host(a)[:n], fkv.to_host(b)[:n])
+    n_seg = int(fkv.to_host(ckv.seg_off)[-1])
+    for a, b, cnt in ((ckv.k, ckv2.k, n), (ckv.v, ckv2.v, n),
+                      (ckv.tok_off, ckv2.tok_off, None), (ckv.seg_off, ckv2.seg_off, None),
+                      (ckv.seg_idx, ckv2.seg_idx, n_seg)):
+        assert np.array_equal(fkv.to_host(a)[:cnt], fkv.to_host(b)[:cnt])
     assert all(t > 0 for t in ms), ms
     role0 = np.zeros(w.num_heads, dtype=np.uint8)
     ckv3 = fkv.CompressedKV(desc, role0, inp.static_keep_mask, w.budget_m)
