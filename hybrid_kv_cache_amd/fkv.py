@@ -5,9 +5,9 @@ current torch stream becomes the hipStream_t; every step of the path runs in
 the library's HIP kernels.  Loading fails loudly when the library has not
 been built (``python -m hybrid_kv_cache_amd.build``); there is no fallback.
 
-Names mirror the C ABI: fkv_plan, fkv_compress, fkv_attend, fkv_attend_dense,
-fkv_status_str, fkv_last_error.  ``CompressedKV`` allocates the ragged cache
-and workspace for one layer with torch.
+Names mirror the C ABI (EXPORTED below).  ``CompressedKV`` allocates one
+layer's ragged cache and workspaces with torch; ``RollingCache`` carries a
+layer's compressed cache across chunk steps.
 """
 from __future__ import annotations
 
@@ -24,13 +24,14 @@ FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
 FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
-EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_timed", "fkv_plan_ragged",
-            "fkv_compress_ragged",
-            "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
-            "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
-            "fkv_profile_workspace",
-            "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
-            "fkv_attend", "fkv_attend_dense", "fkv_status_str", "fkv_last_error")
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_timed",
+            "fkv_plan_ragged", "fkv_compress_ragged", "fkv_refresh_current",
+            "fkv_roll_static_mask",
+            "fkv_plan_tokens", "fkv_compress_tokens",
+            "fkv_compress_fp8", "fkv_attend_fp8",
+            "fkv_profile_workspace", "fkv_profile_heads", "fkv_classify_heads",
+            "fkv_attend_workspace", "fkv_attend", "fkv_attend_dense",
+            "fkv_status_str", "fkv_last_error")
 
 
 class FkvDesc(ctypes.Structure):
@@ -47,6 +48,11 @@ class FkvCkv(ctypes.Structure):
                 ("cap_tokens", ctypes.c_int64)]
 
 
+class FkvTokenCfg(ctypes.Structure):
+    _fields_ = [("sink_frames", ctypes.c_int32), ("recent_frames", ctypes.c_int32),
+                ("budget_tokens", ctypes.c_int32), ("boundary_tokens", ctypes.c_int32)]
+
+
 class FkvError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"fkv status {status}: {detail}")
@@ -54,11 +60,6 @@ class FkvError(RuntimeError):
 
 
 _lib = None
-
-
-class FkvTokenCfg(ctypes.Structure):
-    _fields_ = [("sink_frames", ctypes.c_int32), ("recent_frames", ctypes.c_int32),
-                ("budget_tokens", ctypes.c_int32), ("boundary_tokens", ctypes.c_int32)]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
