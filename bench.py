@@ -322,6 +322,19 @@ def kernel_rates(r):
             "attend_frac_of_peak": k4_tf / BF16_PEAK_TFLOPS}
 
 
+def measured_peaks(fkv, torch):
+    """The roofline denominators measured on this device: the sustained bf16
+    MFMA rate (fkv_mfma_peak: chained 32x32x16 MFMAs on register operands)
+    and a device-to-device copy of 1 GiB (bytes read + written / time)."""
+    tf = fkv.fkv_mfma_peak()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_loop(lambda _: dst.copy_(src), [None], 10, 2, torch)
+    del src, dst
+    return {"mfma_bf16_tflops": tf, "hbm_copy_gbs": 2.0 * (1 << 30) / (ms * 1e-3) / 1e9,
+            "datasheet_bf16_tflops": BF16_PEAK_TFLOPS, "datasheet_hbm_gbs": HBM_PEAK_GBS}
+
+
 def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
     """The oracle as it stands, timed on this host over the whole layer
     (scoring, selection, compaction and attention of every query row),
@@ -452,6 +465,10 @@ def main():
         line["token_variant"] = measure_tokens(w.name, args, fkv, torch, W)
         line["fp8_cache"] = [measure_fp8(n, args, fkv, torch, W)
                              for n in (w.name, args.secondary) if n]
+    if w.dtype == "bf16":
+        line["measured_peaks"] = measured_peaks(fkv, torch)
+        line["roofline_frac_of_measured_peak"] = (
+            line["roofline"]["achieved"] / line["measured_peaks"]["mfma_bf16_tflops"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
     else:

@@ -19,6 +19,11 @@
 #include "fkv_launch.h"
 #include "fkv_fp8.h"
 
+namespace fkv {
+// calib.hip: `blocks` 256-thread workgroups, 8 x iters MFMAs per wave.
+hipError_t launch_mfma_peak(float *sink, int blocks, int iters, hipStream_t s);
+}  // namespace fkv
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -809,6 +814,36 @@ fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void 
     return fail(FKV_ERR_NULL, "q, k_cache, v_cache or out is NULL");
   return attend_common(desc, q, k_cache, v_cache, nullptr, out, workspace, workspace_bytes,
                        stream);
+}
+
+fkv_status_t fkv_mfma_peak(int32_t iters, float *sink, double *tflops) {
+  if (!sink || !tflops) return fail(FKV_ERR_NULL, "sink or tflops is NULL");
+  if (iters < 1) return fail(FKV_ERR_SHAPE, "iters %d < 1", iters);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  hipEvent_t ev[2] = {};
+  if ((e = hipEventCreate(&ev[0])) != hipSuccess) return hip_fail(e, "event creation");
+  if ((e = hipEventCreate(&ev[1])) != hipSuccess) {
+    hipEventDestroy(ev[0]);
+    return hip_fail(e, "event creation");
+  }
+  const int blocks = 2 * cus;
+  e = fkv::launch_mfma_peak(sink, blocks, 10, nullptr);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(ev[0], nullptr);
+  if (e == hipSuccess) e = fkv::launch_mfma_peak(sink, blocks, iters, nullptr);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], nullptr);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  hipEventDestroy(ev[0]);
+  hipEventDestroy(ev[1]);
+  if (e != hipSuccess) return hip_fail(e, "MFMA calibration");
+  // 4 waves per workgroup, 8 MFMAs of 32 x 32 x 16 (2 FLOP each) per iteration
+  const double flop = (double)blocks * 4 * 8 * iters * 2.0 * 32 * 32 * 16;
+  *tflops = flop / (ms * 1e-3) / 1e12;
+  return ok();
 }
 
 const char *fkv_status_str(fkv_status_t status) {

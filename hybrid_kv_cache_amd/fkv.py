@@ -31,7 +31,7 @@ EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_timed",
             "fkv_compress_fp8", "fkv_attend_fp8",
             "fkv_profile_workspace", "fkv_profile_heads", "fkv_classify_heads",
             "fkv_attend_workspace", "fkv_attend", "fkv_attend_dense",
-            "fkv_status_str", "fkv_last_error")
+            "fkv_mfma_peak", "fkv_status_str", "fkv_last_error")
 
 
 class FkvDesc(ctypes.Structure):
@@ -104,6 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "fkv_profile_heads", "fkv_classify_heads", "fkv_attend_workspace",
                  "fkv_attend", "fkv_attend_dense"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.fkv_mfma_peak.argtypes = [I32, P, ctypes.POINTER(ctypes.c_double)]
+    lib.fkv_mfma_peak.restype = ctypes.c_int
     lib.fkv_status_str.argtypes = [ctypes.c_int]
     lib.fkv_status_str.restype = ctypes.c_char_p
     lib.fkv_last_error.argtypes = []
@@ -392,6 +394,16 @@ def fkv_attend_dense(desc: FkvDesc, q, k_cache, v_cache, out, workspace=None,
     ws, ws_bytes = _ws(workspace)
     _check(lib.fkv_attend_dense(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(out), ws, ws_bytes, _stream(stream)))
+
+
+def fkv_mfma_peak(iters: int = 4000) -> float:
+    """Measured sustained bf16 MFMA rate of the current device, TFLOP/s."""
+    import torch
+    lib = load()
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = ctypes.c_double(0.0)
+    _check(lib.fkv_mfma_peak(int(iters), _ptr(sink), ctypes.byref(out)))
+    return float(out.value)
 
 
 def fkv_status_str(status: int) -> str:

@@ -295,6 +295,13 @@ fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void 
                               const void *v_cache, void *out, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Roofline calibration: the sustained bf16 MFMA rate of this device, from
+ * chains of 32x32x16 MFMAs on register operands (two 4-wave workgroups per
+ * CU, 8 * iters MFMAs per wave) on the default stream; waits for the device.
+ * sink: any device buffer of 4 bytes (written only to keep the chains
+ * alive, in practice never).  *tflops receives TFLOP/s. */
+fkv_status_t fkv_mfma_peak(int32_t iters, float *sink, double *tflops);
+
 /* Static text for a status code. */
 const char *fkv_status_str(fkv_status_t status);
 

@@ -265,3 +265,10 @@ def test_compress_timed_matches_compress():
     ckv3 = fkv.CompressedKV(desc, role0, inp.static_keep_mask, w.budget_m)
     ms0 = fkv.fkv_compress_timed(desc, q, k, v, role0, inp.static_keep_mask, w.budget_m, ckv3)
     assert ms0[1] > 0 and ms0[2] > 0 and ms0[0] < ms[0]
+
+
+def test_mfma_peak_calibration_is_plausible():
+    """The calibration kernel reports a bf16 MFMA rate between half and the
+    whole of the datasheet's 2.5 PFLOP/s."""
+    tf = fkv.fkv_mfma_peak(iters=2000)
+    assert 1250.0 < tf <= 2600.0, tf
