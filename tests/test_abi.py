@@ -343,3 +343,10 @@ def test_plan_tokens_errors(lib):
     assert lib.fkv_compress_tokens(ctypes.byref(d), ctypes.byref(cfg), 0x10, 0x20, 0x30,
                                    role.ctypes.data, ctypes.byref(out), None, 0x40, 1 << 20,
                                    None) == fkv.FKV_ERR_CAPACITY
+
+
+def test_mfma_peak_argument_errors(lib):
+    out = ctypes.c_double(0.0)
+    assert lib.fkv_mfma_peak(100, None, ctypes.byref(out)) == fkv.FKV_ERR_NULL
+    assert lib.fkv_mfma_peak(100, 0x1000, None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_mfma_peak(0, 0x1000, ctypes.byref(out)) == fkv.FKV_ERR_SHAPE
