@@ -272,3 +272,54 @@ def test_mfma_peak_calibration_is_plausible():
     whole of the datasheet's 2.5 PFLOP/s."""
     tf = fkv.fkv_mfma_peak(iters=2000)
     assert 1250.0 < tf <= 2600.0, tf
+
+
+def test_no_writes_past_the_outputs():
+    """Every output buffer gets 4 KiB of sentinel bytes past its end: the
+    compressed K/V (bf16 and e4m3), offsets, selection, scores, attention
+    output and the token variant's row sources are written only within their
+    documented extent."""
+    import torch
+    w = W.small_workload(tokens_per_frame=100, num_heads=5, hist_frames=9, budget_m=4,
+                         num_static=2, query_stride=3, seed=71)
+    inp = W.generate_layer(w)
+    desc = fkv.desc_for(w)
+    q, k, v = fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v)
+    pad = 4096
+
+    def padded(t, n_elems):
+        """A flat tensor of n_elems + pad bytes' worth, sentinel-filled, and its head view."""
+        per = t.element_size()
+        raw = torch.full((n_elems * per + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        return raw, raw[:n_elems * per].view(t.dtype)
+
+    ckv = fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m)
+    raws = []
+    for name in ("k", "v", "tok_off", "seg_idx", "seg_off", "seg_score"):
+        t = getattr(ckv, name)
+        raw, view = padded(t, t.numel())
+        setattr(ckv, name, view.view(t.shape))
+        raws.append((name, raw, t.numel() * t.element_size()))
+    fkv.fkv_compress(desc, q, k, v, inp.head_role, inp.static_keep_mask, w.budget_m, ckv)
+    out_raw, out = padded(torch.empty(0, dtype=torch.bfloat16), w.n_q * w.num_heads * w.head_dim)
+    fkv.fkv_attend(desc, q, ckv, out.view(w.n_q, w.num_heads, w.head_dim))
+    # e4m3 cache
+    c8 = fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m, fp8=True)
+    for name in ("k", "v"):
+        t = getattr(c8, name)
+        raw, view = padded(t, t.numel())
+        setattr(c8, name, view.view(t.shape))
+        raws.append(("fp8 " + name, raw, t.numel()))
+    sc = np.full(w.num_heads, 0.02, dtype=np.float32)
+    fkv.fkv_compress_fp8(desc, q, k, v, inp.head_role, inp.static_keep_mask, w.budget_m, sc,
+                         sc, c8)
+    # token variant row sources
+    cfg = fkv.FkvTokenCfg(1, 2, 150, 20)
+    ct = fkv.CompressedKV(desc, inp.head_role, None, 0, token_cfg=cfg)
+    src_raw, src = padded(torch.empty(0, dtype=torch.int32), ct.kept_tokens)
+    fkv.fkv_compress_tokens(desc, cfg, q, k, v, inp.head_role, ct, src)
+    torch.cuda.synchronize()
+    for name, raw, nbytes in raws + [("out", out_raw, out.numel() * 2),
+                                      ("row_src", src_raw, ct.kept_tokens * 4)]:
+        tail = fkv.to_host(raw)[nbytes:]
+        assert (tail == 0xA5).all(), f"{name}: bytes written past the end"
