@@ -242,6 +242,16 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
         int v = cvt2<false>(p0, p1, 0);
         pf[4 * kb + t] = cvt2<true>(p2, p3, v);
       }
+    // Score MFMAs of the next tile interleaved with this tile's softmax:
+    // K-fragment reads four ahead, then per MFMA one read and a slice of
+    // the weights.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -255,6 +265,14 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
       o[db] = mfma_fp8(vf, pf, o[db]);
     }
     lsum = mfma_fp8(ones, pf, lsum);
+    // Value product: transposing reads eight ahead, two per MFMA after that.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
   if (ntiles > 0) {
