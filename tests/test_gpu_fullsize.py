@@ -48,8 +48,9 @@ def test_480p_layer():
     check_layer(W.WORKLOADS["480p_layer"], 0)
 
 
-@pytest.mark.parametrize("layer", [0, 29])
+@pytest.mark.parametrize("layer", range(30))
 def test_480p_30layers(layer):
+    """Every layer of the 30-layer 480P pass (own seed, head roles, masks)."""
     check_layer(W.WORKLOADS["480p_30layers"], layer)
 
 
