@@ -335,6 +335,27 @@ def measured_peaks(fkv, torch):
             "datasheet_bf16_tflops": BF16_PEAK_TFLOPS, "datasheet_hbm_gbs": HBM_PEAK_GBS}
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def numpy_blas() -> str:
+    """Name and version of the BLAS NumPy was built against."""
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '?')}"
+    except Exception:
+        return "unknown"
+
+
 def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
     """The oracle as it stands, timed on this host over the whole layer
     (scoring, selection, compaction and attention of every query row),
@@ -359,6 +380,7 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
         reps += 1
     return {"value": reps * w.n_q / (t_comp + t_attn), "unit": "query tok/s per layer",
             "cores": int(cores), "kind": "oracle",
+            "cpu_model": host_cpu_model(), "blas": numpy_blas(),
             "sample": f"{w.name}: {reps} full layer pass(es), all {w.n_q} query rows: "
                       f"compress (score+select+compact) {t_comp:.1f} s + attention "
                       f"{t_attn:.1f} s; float64 NumPy"}

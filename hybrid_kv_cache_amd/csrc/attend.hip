@@ -22,6 +22,7 @@
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace fkv {
@@ -526,12 +527,22 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
 }  // namespace
 
 namespace {
+// Compute units of the current device, looked up once per device: the
+// attention calls ask for it on every launch.
 int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 0;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 }  // namespace

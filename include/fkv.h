@@ -89,12 +89,14 @@ typedef struct fkv_ckv {
   int64_t cap_tokens;  /* rows available in k and v                            */
 } fkv_ckv_t;
 
-/* Host-only planning.  The kept counts depend only on the roles, the static
- * mask and the budget, so the compressed size is known before any data is
- * read.  head_role [H] and static_keep_mask [H * F_h] (row-major; rows of
- * dynamic heads ignored) are host arrays.  Writes the rows the compressed
- * cache needs (tok_off[H]) to *kept_tokens and the workspace bytes
- * fkv_compress needs to *workspace_bytes.  Either output pointer may be NULL.
+/* Host-only planning ([S] 关键模块 2: a static head's reduction is fixed in
+ * size once profiling has frozen its pattern; 关键模块 3: a dynamic head keeps
+ * a fixed number of top segments).  The kept counts therefore depend only on
+ * the roles, the static mask and the budget, so the compressed size is known
+ * before any data is read.  head_role [H] and static_keep_mask [H * F_h]
+ * (row-major; rows of dynamic heads ignored) are host arrays.  Writes the
+ * rows the compressed cache needs (tok_off[H]) to *kept_tokens and the
+ * workspace bytes fkv_compress needs to *workspace_bytes.  Either output pointer may be NULL.
  * A budget above F_h keeps every history frame of a dynamic head. */
 fkv_status_t fkv_plan(const fkv_desc_t *desc, const uint8_t *head_role,
                       const uint8_t *static_keep_mask, int32_t budget_m,
@@ -269,7 +271,13 @@ fkv_status_t fkv_classify_heads(const fkv_desc_t *desc, const float *mass_sum, i
                                 float threshold, uint8_t *head_role, uint8_t *static_keep_mask,
                                 float *discontinuity);
 
-/* Bytes of the optional attention workspace for the current HIP device: the
+/* Attention workspace.  The method's attention call takes only the queries
+ * and the compressed cache; the (workspace, workspace_bytes) pair of
+ * fkv_attend and fkv_attend_dense is an addition of this library, optional
+ * (NULL, 0 is always accepted) and used only to balance the work of
+ * underfilled launches across the compute units.
+ *
+ * Bytes of the optional attention workspace for the current HIP device: the
  * bf16 attention can then split its work into equal parts, one per resident
  * workgroup (two per compute unit), whatever the number of (head, 128-query)
  * tiles, and merges the pieces of tiles that the split cuts through partial
@@ -288,9 +296,11 @@ fkv_status_t fkv_attend_workspace(const fkv_desc_t *desc, size_t *workspace_byte
 fkv_status_t fkv_attend(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
                         void *out, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Full-KV baseline: the same attention kernel over the whole uncompressed
- * window (every query sees all N_win keys of its head).  workspace as for
- * fkv_attend. */
+/* Full-KV baseline ([S] 实验 › 实验设计: the method is measured against
+ * keeping every history frame's KV): the same attention kernel over the whole
+ * uncompressed window, every query seeing all N_win keys of its head.
+ * q, k_cache, v_cache as for fkv_compress; out as for fkv_attend; workspace
+ * as for fkv_attend (optional, an addition of this library). */
 fkv_status_t fkv_attend_dense(const fkv_desc_t *desc, const void *q, const void *k_cache,
                               const void *v_cache, void *out, void *workspace,
                               size_t workspace_bytes, void *stream);
