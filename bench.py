@@ -12,6 +12,10 @@ To keep the 256 MB last-level cache from holding a 480P layer's whole window
 between steps, the timed loop walks over several device copies of the layer
 (--copies), so K/V come from HBM as they would in a multi-layer pass.
 
+The multi-layer passes (the 30-layer 480P pass and the 40-layer 720P pass of
+a 14B-class model) are timed with every layer's inputs and compressed cache
+resident in HBM at once ("multi_layer").
+
 Also reported (same workload): the rolling compressed cache at its settled
 size ("rolling"), head profiling over every query of a sample
 ("head_profiling"), the token-granular variant ("token_variant"), the e4m3
@@ -54,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rolling", action="store_true",
                     help="skip the rolling-cache measurement")
+    ap.add_argument("--multilayer", default="480p_30layers,720p_14b_40layers",
+                    help="multi-layer passes to time with every layer resident "
+                         "(comma-separated workload names, '' to skip)")
     ap.add_argument("--profile-only", action="store_true",
                     help="run the timed loop only (for rocprofv3), print nothing else")
     ap.add_argument("--only", choices=["step", "compress", "attend", "dense", "copy"],
@@ -153,6 +160,64 @@ def measure(wname, args, fkv, torch, W):
                 compact_bytes=4.0 * kept * D * elt,
                 kept_frac_hist=(kept / w.num_heads / w.tokens_per_frame - w.cur_frames)
                 / max(w.hist_frames, 1))
+
+
+def measure_multilayer(wname, args, fkv, torch, W, reps):
+    """A whole multi-layer pass with every layer resident in HBM: one chunk
+    step of all layers (fkv_compress + fkv_attend per layer, in layer order),
+    the same pass's attention alone, and the full-KV attention pass
+    (fkv_attend_dense per layer).  Layers are generated on the host by a few
+    threads (NumPy releases the interpreter lock in its array loops) and
+    uploaded as they are ready."""
+    import concurrent.futures as cf
+    w = W.WORKLOADS[wname]
+    layers = [None] * w.num_layers
+    t0 = time.perf_counter()
+    workers = max(1, min(8, len(os.sched_getaffinity(0)) // 2))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {ex.submit(W.generate_layer, w, l): l for l in range(w.num_layers)}
+        for f in cf.as_completed(futs):
+            l = futs[f]
+            layers[l] = Layer(w, f.result(), fkv, torch)
+            del futs[f]
+    gen_s = time.perf_counter() - t0
+
+    def run_pass(fn):
+        for L in layers:
+            fn(L)
+
+    def step(L):
+        fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
+        fkv.fkv_attend(L.desc, L.q, L.ckv, L.out)
+
+    ms_pass = time_loop(lambda _: run_pass(step), [None], reps, 1, torch)
+    ms_attend = time_loop(lambda _: run_pass(lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv,
+                                                                      L.out)),
+                          [None], reps, 1, torch)
+    ms_dense = time_loop(lambda _: run_pass(lambda L: fkv.fkv_attend_dense(
+        L.desc, L.q, L.k, L.v, L.dout, L.ckv.attend_ws)), [None], reps, 1, torch)
+    rows = sum(L.ckv.kept_tokens for L in layers)
+    n = w.num_layers
+    flop = 4.0 * w.n_q * w.head_dim * rows
+    elt = 2 if w.dtype == "bf16" else 4
+    resident = sum(t.numel() * t.element_size()
+                   for L in layers for t in (L.q, L.k, L.v, L.ckv.k, L.ckv.v, L.out, L.dout))
+    out = {"workload": w.name, "layers": n, "passes_timed": reps,
+           "value": w.n_q * n / (ms_pass * 1e-3), "unit": "query tok/s per layer",
+           "ms_per_pass": ms_pass, "ms_per_layer": ms_pass / n,
+           "ms_attend_pass": ms_attend, "ms_full_kv_attend_pass": ms_dense,
+           "attend_tflops": flop / (ms_attend * 1e-3) / 1e12,
+           "attend_frac_of_peak": flop / (ms_attend * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "speedup_vs_full_kv": ms_dense / ms_pass,
+           "attention_speedup_vs_full_kv": ms_dense / ms_attend,
+           "kept_fraction_of_history_kv":
+               (rows / n / w.num_heads / w.tokens_per_frame - w.cur_frames) / w.hist_frames,
+           "cache_bytes_full": 2.0 * n * w.n_win * w.num_heads * w.head_dim * elt,
+           "cache_bytes_compressed": 2.0 * rows * w.head_dim * elt,
+           "hbm_resident_bytes": float(resident), "host_generation_s": gen_s}
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_rolling(wname, args, fkv, torch, W, n_chunks=8):
@@ -487,6 +552,10 @@ def main():
         line["token_variant"] = measure_tokens(w.name, args, fkv, torch, W)
         line["fp8_cache"] = [measure_fp8(n, args, fkv, torch, W)
                              for n in (w.name, args.secondary) if n]
+    if w.dtype == "bf16" and args.multilayer and args.layers <= 1:
+        line["multi_layer"] = [measure_multilayer(n, args, fkv, torch, W,
+                                                  reps=5 if W.WORKLOADS[n].num_layers <= 30 else 3)
+                               for n in args.multilayer.split(",") if n]
     if w.dtype == "bf16":
         line["measured_peaks"] = measured_peaks(fkv, torch)
         line["roofline_frac_of_measured_peak"] = (

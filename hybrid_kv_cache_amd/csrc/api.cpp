@@ -227,13 +227,8 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
   return ok();
 }
 
-// Scoring, selection and compaction of one layer over the window `win`
-// (plain or rolling) with the plan p.
-// kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
-fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
-                             const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
-                             size_t workspace_bytes, void *stream,
-                             const float *kv_scales = nullptr, hipEvent_t *ev = nullptr) {
+// The query pointer and the output cache of a compression with plan p.
+fkv_status_t check_compress_out(const Plan &p, const void *q, const fkv_ckv_t *out) {
   if (!q) return fail(FKV_ERR_NULL, "q is NULL");
   if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
   if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
@@ -241,6 +236,18 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   if (out->cap_tokens < p.tok_off[p.H])
     return fail(FKV_ERR_CAPACITY, "cap_tokens %lld < %lld rows needed",
                 (long long)out->cap_tokens, (long long)p.tok_off[p.H]);
+  return FKV_OK;
+}
+
+// Scoring, selection and compaction of one layer over the window `win`
+// (plain or rolling) with the plan p.
+// kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
+fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
+                             const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
+                             size_t workspace_bytes, void *stream,
+                             const float *kv_scales = nullptr, hipEvent_t *ev = nullptr) {
+  fkv_status_t st = check_compress_out(p, q, out);
+  if (st != FKV_OK) return st;
   if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
     return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
@@ -266,6 +273,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     sa.n_s = p.n_s;
     sa.stride = p.s;
     sa.n_dyn = p.n_dyn;
+    sa.n_qb = 0;
     sa.c = c;
     std::memcpy(sa.dyn_heads, p.dyn_heads, sizeof(sa.dyn_heads));
     std::memcpy(sa.fh, p.fh, sizeof(sa.fh));
@@ -725,6 +733,7 @@ fkv_status_t fkv_profile_heads(const fkv_desc_t *desc, const void *q, const void
   sa.n_s = (n_q + desc->query_stride - 1) / desc->query_stride;
   sa.stride = desc->query_stride;
   sa.n_dyn = H;
+  sa.n_qb = 0;
   sa.c = log2e_scale(*desc);
   for (int h = 0; h < fkv::kMaxHeads; ++h) {
     sa.dyn_heads[h] = h < H ? h : 0;

@@ -45,6 +45,7 @@ struct ScoreArgs {
   WinView win;
   float *lse;           // [n_dyn, n_s, F_tot]
   int32_t H, D, T, F_c, F_tot, n_s, stride, n_dyn;
+  int32_t n_qb;         // blocks of sampled queries per (head, frame) (set by the launcher)
   float c;
   int32_t dyn_heads[kMaxHeads];
   int32_t fh[kMaxHeads];

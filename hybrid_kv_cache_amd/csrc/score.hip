@@ -49,15 +49,26 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  const int di = blockIdx.z;
+  // Work unit u = (dynamic head di, window frame f), u = di * F_tot + f,
+  // split into n_qb blocks of 128 sampled queries that all read the frame's
+  // K.  Workgroups go to the 8 XCDs round-robin (workgroup b runs on XCD
+  // b % 8), so unit u is given to XCD u % 8 and its query blocks to
+  // consecutive workgroups of that XCD: they run together and the frame's K
+  // comes from HBM once, then from the XCD's L2.
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int lu = slot / a.n_qb, qb = slot - lu * a.n_qb;
+  const int u = lu * 8 + xcd;
+  if (u >= a.n_dyn * a.F_tot) return;  // padding of the last round of units
+  const int di = u / a.F_tot;
+  const int f = u - di * a.F_tot;
   // The head index is read from a kernel-argument array with a runtime
   // index; readfirstlane tells the compiler it is wave-uniform, so the K
   // buffer resource stays in scalar registers.
   const int h = __builtin_amdgcn_readfirstlane(a.dyn_heads[di]);
   const int fh_h = __builtin_amdgcn_readfirstlane(a.fh[h]);
-  const int f = blockIdx.y;
   if (f >= fh_h + a.F_c) return;  // beyond this head's window
-  const int r = blockIdx.x * kBM + wave * 32 + col;   // sampled row
+  const int r = qb * kBM + wave * 32 + col;   // sampled row
   const int64_t hd = (int64_t)a.H * kD;
 
   bf16x8 qf[8];
@@ -232,10 +243,14 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
 
 }  // namespace
 
-hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s) {
-  if (a.D != kD) return hipErrorInvalidValue;
-  dim3 grid((a.n_s + kBM - 1) / kBM, a.F_tot, a.n_dyn);
-  hipLaunchKernelGGL(score_bf16_kernel, grid, dim3(256), 0, s, a);
+hipError_t launch_score_bf16(const ScoreArgs &a0, hipStream_t s) {
+  if (a0.D != kD) return hipErrorInvalidValue;
+  ScoreArgs a = a0;
+  a.n_qb = (a.n_s + kBM - 1) / kBM;
+  const int64_t units = (int64_t)a.n_dyn * a.F_tot;
+  const int64_t blocks = (units + 7) / 8 * 8 * a.n_qb;
+  if (units <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(score_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

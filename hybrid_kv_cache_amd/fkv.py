@@ -17,7 +17,10 @@ from typing import Optional
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfkv.so")
+# FKV_LIB names another build of the same library (the host-sanitizer build
+# that the ABI tests also run against); by default the in-tree libfkv.so.
+LIB_PATH = os.environ.get("FKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libfkv.so")
 
 FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
     FKV_ERR_CAPACITY, FKV_ERR_WORKSPACE, FKV_ERR_HIP = range(8)
@@ -96,7 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
-    for name in ("fkv_plan", "fkv_compress", "fkv_compress_timed", "fkv_plan_ragged",
+    for name in ("fkv_plan", "fkv_compress", "fkv_compress_timed",
+                 "fkv_plan_ragged",
                  "fkv_compress_ragged",
                  "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
                  "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",

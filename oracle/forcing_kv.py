@@ -87,11 +87,15 @@ def frame_masses(q_h: np.ndarray, k_h: np.ndarray, tokens_per_frame: int,
     rows = sampled_query_rows(q_h.shape[0], stride)
     n_win = k_h.shape[0]
     n_frames = n_win // tokens_per_frame
-    z = (q_h[rows] @ k_h.T) * scale
-    z = z - z.max(axis=1, keepdims=True)
-    e = np.exp(z)
-    p = e / e.sum(axis=1, keepdims=True)
-    return p.reshape(len(rows), n_frames, tokens_per_frame).sum(axis=2)
+    # the steps below work in place on one [n_s, N_win] array (the same
+    # operations in the same order as z = scale * q k^T; z -= max; p = e^z /
+    # sum e^z), to keep memory and time down at the largest window sizes
+    z = q_h[rows] @ k_h.T
+    z *= scale
+    z -= z.max(axis=1, keepdims=True)
+    np.exp(z, out=z)
+    z /= z.sum(axis=1, keepdims=True)
+    return z.reshape(len(rows), n_frames, tokens_per_frame).sum(axis=2)
 
 
 def segment_scores(q: np.ndarray, k: np.ndarray, head_role: np.ndarray,
@@ -207,17 +211,16 @@ def attend(q: np.ndarray, k_c: np.ndarray, v_c: np.ndarray, tok_off: np.ndarray,
     [len(rows) or Nq, H, D] float64.
     """
     qf = as_f64(q)
-    kc = as_f64(k_c)
-    vc = as_f64(v_c)
     H, D = qf.shape[1], qf.shape[2]
     sc = logit_scale(D, scale)
     sel = np.arange(qf.shape[0]) if rows is None else np.asarray(rows)
     out = np.empty((len(sel), H, D), dtype=np.float64)
     for h in range(H):
         lo, hi = int(tok_off[h]), int(tok_off[h + 1])
+        kc, vc = as_f64(k_c[lo:hi]), as_f64(v_c[lo:hi])   # this head's rows, exact
         for b in range(0, len(sel), block):
             r = sel[b:b + block]
-            out[b:b + block, h] = softmax_attention(qf[r, h], kc[lo:hi], vc[lo:hi], sc)
+            out[b:b + block, h] = softmax_attention(qf[r, h], kc, vc, sc)
     return out
 
 
@@ -225,16 +228,15 @@ def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float = 0.0
                  rows: Optional[np.ndarray] = None, block: int = 1024) -> np.ndarray:
     """Full-KV baseline: every query attends over the whole uncompressed window."""
     qf = as_f64(q)
-    kf = as_f64(k)
-    vf = as_f64(v)
     H, D = qf.shape[1], qf.shape[2]
     sc = logit_scale(D, scale)
     sel = np.arange(qf.shape[0]) if rows is None else np.asarray(rows)
     out = np.empty((len(sel), H, D), dtype=np.float64)
     for h in range(H):
+        kf, vf = as_f64(k[:, h]), as_f64(v[:, h])           # this head's keys, exact
         for b in range(0, len(sel), block):
             r = sel[b:b + block]
-            out[b:b + block, h] = softmax_attention(qf[r, h], kf[:, h], vf[:, h], sc)
+            out[b:b + block, h] = softmax_attention(qf[r, h], kf, vf, sc)
     return out
 
 

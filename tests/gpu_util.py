@@ -10,6 +10,19 @@ from oracle import forcing_kv as O
 # Output tolerances: bf16 inputs with fp32 accumulation / fp32 inputs.
 BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3
 F32_MAX_ABS = 1e-4
+# Beside the absolute bars, the error of every output row (one query of one
+# head, D values) relative to that row's norm.  bf16: the output rounding
+# alone is up to 2^-9 relative per element and the softmax weights are
+# rounded to bf16 for the value product (2^-9 each, averaging out), so rows
+# come out near 2e-3; one 64-key tile dropped or counted twice moves the rows
+# of its query tile by several percent, far above 1e-2.  fp32: all arithmetic
+# in fp32, rows near 1e-6.
+BF16_ROW_REL, F32_ROW_REL = 1e-2, 1e-4
+# Frame scores (mean softmax mass): the GPU sums exact bf16 products in fp32
+# and works in base 2 with fp32 log-sum-exps; each mass comes out within a few
+# 1e-7 relative of the float64 value, so the tie band of the selection
+# (1e-5 relative) is also the bar for the scores.
+SCORE_RTOL = 1e-5
 
 
 def announce(msg: str) -> None:
@@ -101,20 +114,42 @@ def check_selection(w, res, oracle_scores, role, mask, budget_m):
     return gpu_kept
 
 
-def check_scores(res, oracle_scores, role, rtol=1e-3):
+def check_scores(res, oracle_scores, role, rtol=SCORE_RTOL):
+    """Dynamic heads' scores within rtol of the oracle's (atol only absorbs
+    masses below fp32's normal range); NaN for static heads.  Returns the
+    largest relative error seen."""
     s = res["seg_score"]
+    worst = 0.0
     for h in range(len(role)):
         if role[h] == O.DYNAMIC:
-            np.testing.assert_allclose(s[h], oracle_scores[h], rtol=rtol, atol=1e-7)
+            ref = oracle_scores[h]
+            np.testing.assert_allclose(s[h], ref, rtol=rtol, atol=1e-30)
+            if ref.size:
+                rel = np.abs(s[h] - ref) / np.maximum(np.abs(ref), 1e-30)
+                worst = max(worst, float(rel.max()))
         else:
             assert np.isnan(s[h]).all()
+    announce(f"scores: max relative error {worst:.3e} (bar {rtol:.0e})")
+    return worst
+
+
+def row_rel_error(got, ref):
+    """Per output row (the last axis): ||got - ref|| / ||ref||."""
+    num = np.sqrt(np.sum((got - ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(ref ** 2, axis=-1))
+    return num / np.maximum(den, 1e-300)
 
 
 def check_output(got, ref, dtype):
     err = np.abs(got - ref)
+    rel = row_rel_error(got, ref)
     if dtype == "bf16":
         assert err.max() <= BF16_MAX_ABS, f"max abs err {err.max()}"
         assert err.mean() <= BF16_MEAN_ABS, f"mean abs err {err.mean()}"
+        assert rel.max() <= BF16_ROW_REL, f"row-relative err {rel.max()}"
     else:
         assert err.max() <= F32_MAX_ABS, f"max abs err {err.max()}"
+        assert rel.max() <= F32_ROW_REL, f"row-relative err {rel.max()}"
+    announce(f"output: max abs {err.max():.3e}, mean abs {err.mean():.3e}, "
+             f"max row-relative {rel.max():.3e}")
     return float(err.max()), float(err.mean())

@@ -40,7 +40,7 @@ def test_profile_masses_and_labels(dtype, T, s, seed):
                          num_heads=6, hist_frames=9, num_static=3, query_stride=s, seed=seed)
     samples = [W.generate_profile_sample(w, i) for i in range(2)]
     desc, got, ref = _profile(w, samples)
-    np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-6)
+    np.testing.assert_allclose(got, ref, rtol=G.SCORE_RTOL, atol=1e-12)
     np.testing.assert_allclose(got.sum(axis=1), 2.0, rtol=1e-4)
     # labels: the library's host rule on the GPU masses equals the oracle's
     # rule on the same masses, and both recover the planted static heads
@@ -55,6 +55,6 @@ def test_profile_480p_layer_shape():
     w = W.WORKLOADS["480p_layer"]
     samples = [W.generate_profile_sample(w, 0)]
     desc, got, ref = _profile(w, samples)
-    np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-6)
+    np.testing.assert_allclose(got, ref, rtol=G.SCORE_RTOL, atol=1e-12)
     role, _, _ = fkv.fkv_classify_heads(desc, got, 1, 2.0)
     assert np.array_equal(role, samples[0].head_role)

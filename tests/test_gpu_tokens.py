@@ -16,11 +16,27 @@ def _gpu():
     G.require_gpu()
 
 
-def _check_candidates(gpu_pick, phi, budget, rel=1e-4):
+# Forward error bound of the GPU's fp32 score phi_j = k_j . sum_r q_r: the
+# query sum adds n_s rows and the dot product D products, so with u = 2^-24
+# |phi_gpu - phi| <= (n_s + D) u sum_d |k_jd| sum_r |q_rd| (to first order).
+# 2.5e-5 covers n_s + D up to about 420 (the 480P sample: 293 + 128).
+PHI_BOUND_REL = 2.5e-5
+
+
+def phi_error_bound(q_h, k_cand, query_stride):
+    """Per candidate: PHI_BOUND_REL * sum_d |k_jd| sum_r |q_rd| (float64)."""
+    rows = O.sampled_query_rows(q_h.shape[0], query_stride)
+    a = np.abs(O.as_f64(q_h)[rows]).sum(axis=0)
+    return PHI_BOUND_REL * (np.abs(O.as_f64(k_cand)) @ a)
+
+
+def _check_candidates(gpu_pick, phi, budget, bound):
     """The GPU's kept candidates (local indices) against the oracle's float64
-    scores: every score clearly above the C-th best is kept, none clearly
-    below, C in all (ties inside a band of rel * max |phi| may go either way;
-    the GPU sums in fp32 in another order)."""
+    scores.  A candidate is ambiguous when its score and the C-th best score
+    are within their two error bounds of each other (the GPU may rank such a
+    pair either way); every other candidate above the C-th best must be kept
+    and every other one below it dropped, C in all.  Returns the number of
+    ambiguous candidates."""
     n = len(phi)
     c = min(max(budget, 0), n)
     assert len(gpu_pick) == c and np.all(np.diff(gpu_pick) > 0)
@@ -28,13 +44,14 @@ def _check_candidates(gpu_pick, phi, budget, rel=1e-4):
         assert np.array_equal(gpu_pick, np.arange(c))
         return 0
     order = np.lexsort((np.arange(n), -phi))
-    cut = phi[order[c - 1]]
-    eps = rel * max(np.abs(phi).max(), 1e-30)
+    j_cut = order[c - 1]
+    cut = phi[j_cut]
+    amb = np.abs(phi - cut) <= bound + bound[j_cut]
     picked = np.zeros(n, dtype=bool)
     picked[gpu_pick] = True
-    assert picked[phi > cut + eps].all(), "a clearly better candidate was dropped"
-    assert not picked[phi < cut - eps].any(), "a clearly worse candidate was kept"
-    return int(((phi >= cut - eps) & (phi <= cut + eps)).sum())
+    assert picked[(phi > cut) & ~amb].all(), "a clearly better candidate was dropped"
+    assert not picked[(phi < cut) & ~amb].any(), "a clearly worse candidate was kept"
+    return int(amb.sum())
 
 
 def run_tokens(w, inp, cfg, rows=None):
@@ -57,7 +74,7 @@ def run_tokens(w, inp, cfg, rows=None):
     gsrc = fkv.to_host(src)[:n].astype(np.int64)
     kc, vc = fkv.to_host(ckv.k)[:n], fkv.to_host(ckv.v)[:n]
     lo_c, hi_c = ref["cand"]
-    band = 0
+    band = band_max = 0
     for h in range(w.num_heads):
         a, b = int(tok_off[h]), int(tok_off[h + 1])
         s = gsrc[a:b]
@@ -69,7 +86,10 @@ def run_tokens(w, inp, cfg, rows=None):
             assert np.array_equal(s[:n_sink], r[:n_sink])
             assert np.array_equal(s[len(s) - n_rec - Fc * T:], r[len(r) - n_rec - Fc * T:])
             pick = s[n_sink:len(s) - n_rec - Fc * T] - lo_c
-            band += _check_candidates(pick, ref["phi"][h], cfg.budget_tokens)
+            bound = phi_error_bound(inp.q[:, h], inp.k[lo_c:hi_c, h], w.query_stride)
+            nb = _check_candidates(pick, ref["phi"][h], cfg.budget_tokens, bound)
+            band_max = max(band_max, nb)
+            band += nb
         else:
             assert np.array_equal(s, ref["src"][h]), f"static head {h}"
     # attention over the GPU's cache, against the oracle over the same rows
@@ -79,7 +99,8 @@ def run_tokens(w, inp, cfg, rows=None):
         got = got[rows]
     want = O.attend(inp.q, kc, vc, tok_off, rows=rows)
     G.check_output(got, want, w.dtype)
-    return band
+    G.announce(f"token picks: {band} ambiguous candidates in all, at most {band_max} per head")
+    return band, band_max
 
 
 @pytest.mark.parametrize("dtype,T,cfg,seed", [
@@ -101,7 +122,7 @@ def test_compress_tokens_zero_queries_tie_to_lowest_index():
     the C lowest-index candidates (the radix select's tie rule)."""
     w = W.small_workload(tokens_per_frame=30, num_heads=3, hist_frames=6, num_static=1, seed=46)
     inp = W.generate_layer(w, zero_q=True)
-    band = run_tokens(w, inp, fkv.FkvTokenCfg(1, 1, 33, 4))
+    band, _ = run_tokens(w, inp, fkv.FkvTokenCfg(1, 1, 33, 4))
     assert band > 0   # every candidate sits in the tie band; the exact check is below
     import torch
     desc = fkv.desc_for(w)
@@ -125,4 +146,8 @@ def test_compress_tokens_480p_shape():
     w = W.WORKLOADS["480p_layer"]
     T = w.tokens_per_frame
     rows = np.random.default_rng(47).choice(w.n_q, 48, replace=False)
-    run_tokens(w, W.generate_layer(w), fkv.FkvTokenCfg(1, 3, 9 * T, T // 2), rows=rows)
+    _, band_max = run_tokens(w, W.generate_layer(w), fkv.FkvTokenCfg(1, 3, 9 * T, T // 2),
+                             rows=rows)
+    # 18,720 candidates per dynamic head; the oracle's own scores put 3 to 5
+    # of them within the error bounds of the cutoff
+    assert band_max <= 16
