@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfkv.so")
-SOURCES = ["api.cpp", "score.hip", "select.hip", "compact.hip", "attend.hip", "tokens.hip", "attend_fp8.hip", "calib.hip"]
+SOURCES = ["api.cpp", "score.hip", "select.hip", "compact.hip", "attend.hip", "tokens.hip", "attend_fp8.hip", "calib.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

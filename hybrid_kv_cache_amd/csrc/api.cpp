@@ -19,6 +19,9 @@
 #include "fkv_launch.h"
 #include "fkv_fp8.h"
 
+static_assert(FKV_SCRATCH_BYTES == fkv::kScratchBytes,
+              "fkv.h and fkv_launch.h must agree on the scratch size");
+
 namespace fkv {
 // calib.hip: `blocks` 256-thread workgroups, 8 x iters MFMAs per wave.
 hipError_t launch_mfma_peak(float *sink, int blocks, int iters, hipStream_t s);
@@ -451,6 +454,30 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
                          workspace_bytes, stream);
+}
+
+fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                                  const void *v_cache, const uint8_t *head_role,
+                                  const uint8_t *static_keep_mask, int32_t budget_m,
+                                  const fkv_ckv_t *out, void *stream) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_compress_out(p, q, out);
+  if (st != FKV_OK) return st;
+  if (p.ws_bytes > fkv::kScratchBytes)
+    return fail(FKV_ERR_WORKSPACE,
+                "this layer needs %zu bytes of workspace, more than the %zu bytes of the "
+                "library's scratch memory; use fkv_compress with a caller workspace",
+                p.ws_bytes, fkv::kScratchBytes);
+  void *scratch = nullptr;
+  if (p.ws_bytes > 0) {
+    const hipError_t e = fkv::scratch_address(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "scratch memory address");
+  }
+  return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, scratch,
+                         fkv::kScratchBytes, stream);
 }
 
 namespace {

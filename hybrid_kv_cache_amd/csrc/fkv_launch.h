@@ -137,4 +137,10 @@ size_t attend_part_bytes();
 hipError_t launch_attend_bf16(const AttendArgs &a, void *part, size_t part_bytes, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s);
 
+// Library-owned scratch array of fkv_compress_noalloc (scratch.hip): its size
+// per device, and the device address of the current device's copy (looked up
+// once per device; never the array's host-side name).
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+hipError_t scratch_address(void **ptr);
+
 }  // namespace fkv

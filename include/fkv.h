@@ -26,9 +26,10 @@
  *         4 GiB; element offsets are computed in 64 bits.
  *
  * Threading and streams: calls are stateless apart from the thread-local
- * error string; every device operation is enqueued on the given stream
- * (a hipStream_t passed as void*, NULL = the default stream) and no call
- * waits for the device.  The library allocates no device memory.
+ * error string (and the scratch array of fkv_compress_noalloc); every device
+ * operation is enqueued on the given stream (a hipStream_t passed as void*,
+ * NULL = the default stream) and no call waits for the device.  The library
+ * allocates no device memory.
  *
  * Errors: argument errors are detected on the host before any HIP call and
  * returned as a status; a failed kernel launch returns FKV_ERR_HIP.  Faults
@@ -119,6 +120,21 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
                           const uint8_t *static_keep_mask, int32_t budget_m,
                           const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/* fkv_compress without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a fixed array of
+ * FKV_SCRATCH_BYTES bytes inside the library, one copy per device, kept until
+ * the process ends; the call itself allocates nothing.  A layer whose
+ * workspace (fkv_plan's figure) exceeds FKV_SCRATCH_BYTES gets
+ * FKV_ERR_WORKSPACE.  All calls on one device share that device's array:
+ * calls that overlap on one device (other streams or threads) race, so order
+ * them.  Otherwise the same arguments, results and errors as fkv_compress. */
+#define FKV_SCRATCH_BYTES ((size_t)4 << 20)
+fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                                  const void *v_cache, const uint8_t *head_role,
+                                  const uint8_t *static_keep_mask, int32_t budget_m,
+                                  const fkv_ckv_t *out, void *stream);
 
 /* Measurement helper: fkv_compress with HIP events around its three stages;
  * waits for the device and writes the stage times in milliseconds to ms[3]

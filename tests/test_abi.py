@@ -172,6 +172,38 @@ def test_compress_argument_errors_before_any_hip_call(lib):
     assert "cap_tokens" in _capture_error(d, kept - 1, ws)
 
 
+def test_compress_noalloc_argument_errors_before_any_hip_call(lib):
+    """The allocation-free entry point checks its arguments and its scratch
+    limit on the host: a layer whose workspace exceeds the library's scratch
+    size is refused with a message naming both sizes."""
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    role, mask = np.ones(2, np.uint8), np.zeros((2, 4), np.uint8)
+    st, kept, ws = _plan(d, role, mask, 2)
+    assert st == 0 and ws <= fkv.SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(desc, cap, q=fake, role=role, mask=mask, budget=2):
+        ckv = fkv.FkvCkv(fake, fake, fake, fake, fake, None, cap)
+        r = np.ascontiguousarray(role, np.uint8)
+        m = np.ascontiguousarray(mask, np.uint8)
+        return lib.fkv_compress_noalloc(ctypes.byref(desc), q, fake, fake, r.ctypes.data,
+                                        m.ctypes.data, budget, ctypes.byref(ckv), None)
+
+    assert call(d, kept - 1) == fkv.FKV_ERR_CAPACITY
+    assert call(d, kept, q=None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_compress_noalloc(None, fake, fake, fake, None, None, 2, None,
+                                    None) == fkv.FKV_ERR_NULL
+    # 64 dynamic heads, T = 8160, every query scored: the per-query frame
+    # sums alone need 64 * 24480 * 21 * 4 bytes, far beyond the scratch size
+    big = fkv.make_desc(64, 128, 8160, 18, 3, 1)
+    st, kept_big, ws_big = _plan(big, np.ones(64, np.uint8), np.zeros((64, 18), np.uint8), 12)
+    assert st == 0 and ws_big > fkv.SCRATCH_BYTES
+    assert call(big, kept_big, role=np.ones(64, np.uint8), mask=np.zeros((64, 18), np.uint8),
+                budget=12) == fkv.FKV_ERR_WORKSPACE
+    msg = fkv.fkv_last_error()
+    assert str(ws_big) in msg and str(fkv.SCRATCH_BYTES) in msg
+
+
 def _capture_error(d, cap, ws):
     _compress_status(d, cap, ws)
     return fkv.fkv_last_error()
