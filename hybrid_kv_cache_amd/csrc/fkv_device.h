@@ -46,16 +46,37 @@ __device__ __forceinline__ float swap_halves(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
-// v_permlane32_swap with both operands = v: one result holds v of the lower
-// half in both halves, the other v of the upper half.  Any symmetric
-// combination of the two is the lane-pair (l, l ^ 32) reduction.
+// v_permlane32_swap / v_permlane16_swap applied to two copies of v (rows are
+// 16 lanes, halves 32):
+//   permlane32: a = the lower half of v in both halves, b = the upper half;
+//   permlane16: a = rows [0, 0, 2, 2] of v, b = rows [1, 1, 3, 3].
+// Written in inline assembly: given the same value twice, the compiler's
+// builtin may fold its two results into one (seen with ROCm 7.2), which is
+// wrong for these cross-lane swaps.  The s_nop gives the two wait states that
+// a VALU write of the source registers needs before the swap reads them.
+struct LanePair {
+  uint32_t a, b;
+};
+__device__ __forceinline__ LanePair permlane32_swap_copies(uint32_t v) {
+  uint32_t a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return LanePair{a, b};
+}
+__device__ __forceinline__ LanePair permlane16_swap_copies(uint32_t v) {
+  uint32_t a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return LanePair{a, b};
+}
+
+// Lane-pair (l, l ^ 32) reductions: any symmetric combination of the two
+// halves of a permlane32 swap.
 __device__ __forceinline__ float pair_max(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const LanePair r = permlane32_swap_copies(__float_as_uint(v));
+  return fmaxf(__uint_as_float(r.a), __uint_as_float(r.b));
 }
 __device__ __forceinline__ float pair_sum(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const LanePair r = permlane32_swap_copies(__float_as_uint(v));
+  return __uint_as_float(r.a) + __uint_as_float(r.b);
 }
 
 // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their maxima):

@@ -37,13 +37,15 @@ struct CopySlot {
   int64_t dst_row;
 };
 
-// Per-(dynamic head, sampled query, window frame) log-sum-exp of the scaled
-// logits in base 2: lse[(d * n_s + r) * F_tot + f] = log2 sum_{j in f} 2^(c q.k_j),
+// Per-(dynamic head, window frame, sampled query) log-sum-exp of the scaled
+// logits in base 2: lse[(d * F_tot + f) * n_s + r] = log2 sum_{j in f} 2^(c q.k_j),
 // with c = scale * log2(e), for f < fh[h] + F_c (F_tot: the largest window).
+// Frame-major, so that the selection reads one frame of consecutive queries
+// with coalesced loads.
 struct ScoreArgs {
   const void *q;        // [Nq, H, D]
   WinView win;
-  float *lse;           // [n_dyn, n_s, F_tot]
+  float *lse;           // [n_dyn, F_tot, n_s]
   int32_t H, D, T, F_c, F_tot, n_s, stride, n_dyn;
   int32_t n_qb;         // blocks of sampled queries per (head, frame) (set by the launcher)
   float c;
@@ -52,7 +54,7 @@ struct ScoreArgs {
 };
 
 struct SelectArgs {
-  const float *lse;     // [n_dyn, n_s, F_tot] (unused when n_dyn == 0)
+  const float *lse;     // [n_dyn, F_tot, n_s] (unused when n_dyn == 0)
   int32_t *seg_idx;     // [seg_off[H]]
   int32_t *seg_off;     // [H + 1]
   int64_t *tok_off;     // [H + 1]
@@ -68,7 +70,7 @@ struct SelectArgs {
 };
 
 // Head profiling: per (head, window frame) mean mass over the sampled
-// queries, from the log-sum-exps of all heads (lse [H, n_s, F_tot]), added to
+// queries, from the log-sum-exps of all heads (lse [H, F_tot, n_s]), added to
 // out [H, F_tot].
 struct ProfileArgs {
   const float *lse;

@@ -114,12 +114,17 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
 
   for (int t = 0; t < kAhead; ++t) issue(t);
   float m = kNegBig, l = 0.f;
+  // A wave whose 32 sampled rows all lie past the sample (the tail of the
+  // last query block) keeps its share of the copies and barriers but skips
+  // the arithmetic.
+  const bool active = __builtin_amdgcn_readfirstlane(qb * kBM + wave * 32) < a.n_s;
   for (int it = 0; it < ntiles; ++it) {
     // Tile `it` must have landed; the (at most kAhead - 1) later ones may
     // stay in flight.
     wait_tiles_in_flight(min(kAhead - 1, ntiles - 1 - it));
     __syncthreads();
     issue(it + kAhead);
+    if (!active) continue;
     const char *kl = ring(it);
     const int valid = len - it * kKT;
 
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
   const float m2 = swap_halves(m), l2 = swap_halves(l);
   const float M = fmaxf(m, m2);
   const float L = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
-  if (g == 0 && r < a.n_s) a.lse[((int64_t)di * a.n_s + r) * a.F_tot + f] = M + fast_log2(L);
+  if (g == 0 && r < a.n_s) a.lse[((int64_t)di * a.F_tot + f) * a.n_s + r] = M + fast_log2(L);
 }
 
 // fp32 path (small shapes): one workgroup per (sampled query, dynamic head);
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
         L = L * fast_exp2(M - Mn) + red_l[w] * fast_exp2(red_m[w] - Mn);
         M = Mn;
       }
-      a.lse[((int64_t)di * a.n_s + r) * a.F_tot + f] = M + fast_log2(L);
+      a.lse[((int64_t)di * a.F_tot + f) * a.n_s + r] = M + fast_log2(L);
     }
     __syncthreads();
   }

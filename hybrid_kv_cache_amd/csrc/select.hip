@@ -17,23 +17,65 @@
 // per thread, then over each wave and over the 4 waves in a fixed order
 // (deterministic).
 // Wave 0 then sorts the (score, frame) pairs with a 64-lane bitonic network
-// and marks the first m_eff.  Every head finally writes its seg_idx entries
-// (bit rank = position), its offsets and its compaction slots.
+// (lane exchanges by DPP and permlane swaps, not the LDS crossbar) and marks
+// the first m_eff.  Every head finally writes its seg_idx entries (bit rank =
+// position), its offsets and its compaction slots.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
 namespace fkv {
 namespace {
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// Sum over the 64 lanes of a wave, the total in every lane, without the
+// LDS crossbar: DPP exchanges inside each row of 16 lanes (lane i with i ^ 1,
+// i ^ 2, then the mirrored lane of its half row and of its row), then the
+// row pairs (permlane16 swap) and the two halves (permlane32 swap).  The
+// order of the additions is fixed, so the result is deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp<0xB1>(v);    // quad_perm [1, 0, 3, 2]: lane i ^ 1
+  v += dpp<0x4E>(v);    // quad_perm [2, 3, 0, 1]: lane i ^ 2
+  v += dpp<0x141>(v);   // row_half_mirror: the other quad of the half row
+  v += dpp<0x140>(v);   // row_mirror: the other half row
+  const LanePair r16 = permlane16_swap_copies(__builtin_bit_cast(uint32_t, v));
+  v = __builtin_bit_cast(float, r16.a) + __builtin_bit_cast(float, r16.b);
+  const LanePair r32 = permlane32_swap_copies(__builtin_bit_cast(uint32_t, v));
+  return __builtin_bit_cast(float, r32.a) + __builtin_bit_cast(float, r32.b);
+}
+
+// The value of lane `lane ^ j` (j a power of two below 64; the loops that
+// call it are unrolled, so j is a constant there): xor 1 and 2 by DPP quad
+// permutes, xor 4 and 8 by DPP row shifts (lanes with the bit clear take the
+// lane j above, the others the lane j below, always inside the row of 16),
+// xor 16 and 32 by the permlane swaps of rows and halves.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j, int lane) {
+  const int x = (int)v;
+  switch (j) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);   // row_shl:4
+      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+      return (uint32_t)((lane & 4) ? dn : up);
+    }
+    case 8: {
+      const int up = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0xF, false);   // row_shl:8
+      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+      return (uint32_t)((lane & 8) ? dn : up);
+    }
+    case 16: {
+      const LanePair r = permlane16_swap_copies(v);   // rows [0,0,2,2] / [1,1,3,3]
+      return (lane & 16) ? r.a : r.b;
+    }
+    default: {
+      const LanePair r = permlane32_swap_copies(v);   // halves [lo,lo] / [hi,hi]
+      return (lane & 32) ? r.a : r.b;
+    }
+  }
 }
 
 // (score, idx) a ranks before b: higher score first, then lower index.
@@ -44,10 +86,11 @@ __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib)
 constexpr int kSelWaves = 4;
 
 // Masses of one dynamic head: thread t takes sampled queries t, t + 256, ...;
-// for each, the ft frame log-sum-exps (base 2; rows F_tot apart) become a
-// softmax over the head's window, whose first fh entries (the history) are
-// added to per-thread sums.  The sums are reduced over each wave with
-// shuffles and stored per wave in part[w][f].
+// for each, the ft frame log-sum-exps (base 2; frame f at base[f * n_s + r],
+// so that a wave reads each frame with one coalesced load) become a softmax
+// over the head's window, whose first fh entries (the history) are added to
+// per-thread sums.  The sums are reduced over each wave and stored per wave
+// in part[w][f].
 constexpr int kPartFrames = kMaxHistFrames + kMaxCurFrames;
 
 template <int FT>
@@ -58,10 +101,9 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = 0.f;
   for (int r = tid; r < n_s; r += 64 * kSelWaves) {
-    const float *row = base + (int64_t)r * F_tot;
     float v[FT];
 #pragma unroll
-    for (int f = 0; f < FT; ++f) v[f] = f < ft ? row[f] : -INFINITY;
+    for (int f = 0; f < FT; ++f) v[f] = f < ft ? base[(int64_t)f * n_s + r] : -INFINITY;
     float M = v[0];
 #pragma unroll
     for (int f = 1; f < FT; ++f) M = fmaxf(M, v[f]);
@@ -135,8 +177,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
       for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-          const float os = __shfl_xor(s, j, 64);
-          const int oi = __shfl_xor(idx, j, 64);
+          const float os = __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, s), j, lane));
+          const int oi = (int)lane_xor((uint32_t)idx, j, lane);
           const bool lower = (lane & j) == 0;
           const bool ascending = (lane & k) == 0;
           const bool other_first = ranks_before(os, oi, s, idx);
@@ -153,7 +195,11 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
       const int m_eff = min(a.budget, fh);
       unsigned long long bits = lane < m_eff ? (1ull << idx) : 0ull;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) bits |= __shfl_xor(bits, off, 64);
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = lane_xor((uint32_t)bits, off, lane);
+        const uint32_t hi = lane_xor((uint32_t)(bits >> 32), off, lane);
+        bits |= ((unsigned long long)hi << 32) | lo;
+      }
       if (lane == 0) kept_bits_s = bits;
     }
   }
