@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "fkv.h"
@@ -94,6 +95,13 @@ struct Plan {
   int32_t seg_off[fkv::kMaxHeads + 1];
   int32_t slot_off[fkv::kMaxHeads + 1];
   int64_t tok_off[fkv::kMaxHeads + 1];
+  // Compaction jobs fixed before any score is known (static heads' kept
+  // frames, every head's current chunk) and the rest (dynamic heads' kept
+  // history frames), as prefix sums over heads.
+  int32_t kept[fkv::kMaxHeads];
+  int32_t n_hist_fixed[fkv::kMaxHeads];
+  int32_t fixed_off[fkv::kMaxHeads + 1];
+  int32_t dyn_slot_off[fkv::kMaxHeads + 1];
   size_t ws_lse_off, ws_slot_off, ws_bytes;
 };
 
@@ -135,6 +143,8 @@ fkv_status_t make_plan(const fkv_desc_t *d, const int32_t *hist_frames, const ui
   p->seg_off[0] = 0;
   p->slot_off[0] = 0;
   p->tok_off[0] = 0;
+  p->fixed_off[0] = 0;
+  p->dyn_slot_off[0] = 0;
   for (int h = 0; h < p->H; ++h) {
     int kept;
     p->static_bits[h] = 0;
@@ -162,17 +172,25 @@ fkv_status_t make_plan(const fkv_desc_t *d, const int32_t *hist_frames, const ui
     p->seg_off[h + 1] = p->seg_off[h] + kept;
     p->slot_off[h + 1] = p->slot_off[h] + kept + p->Fc;
     p->tok_off[h + 1] = p->tok_off[h] + (int64_t)(kept + p->Fc) * p->T;
+    p->kept[h] = kept;
+    p->n_hist_fixed[h] = role[h] == FKV_DYNAMIC ? 0 : kept;
+    p->fixed_off[h + 1] = p->fixed_off[h] + p->n_hist_fixed[h] + p->Fc;
+    p->dyn_slot_off[h + 1] = p->dyn_slot_off[h] + (p->dyn_index[h] >= 0 ? kept : 0);
   }
   for (int h = p->n_dyn; h < fkv::kMaxHeads; ++h) p->dyn_heads[h] = 0;
   for (int h = p->H; h < fkv::kMaxHeads; ++h) {
     p->dyn_index[h] = -1;
     p->static_bits[h] = 0;
     p->fh[h] = 0;
+    p->kept[h] = 0;
+    p->n_hist_fixed[h] = 0;
   }
   for (int h = p->H + 1; h <= fkv::kMaxHeads; ++h) {
     p->seg_off[h] = p->seg_off[p->H];
     p->slot_off[h] = p->slot_off[p->H];
     p->tok_off[h] = p->tok_off[p->H];
+    p->fixed_off[h] = p->fixed_off[p->H];
+    p->dyn_slot_off[h] = p->dyn_slot_off[p->H];
   }
   const size_t lse_bytes = p->n_dyn > 0 ? (size_t)p->n_dyn * p->n_s * p->Ft * sizeof(float) : 0;
   p->ws_lse_off = 0;
@@ -197,6 +215,48 @@ fkv::WinView plain_window(const fkv_desc_t *d, const void *k, const void *v) {
 
 fkv_status_t hip_fail(hipError_t e, const char *what) {
   return fail(FKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A second stream per device for the compaction jobs that do not depend on
+// the scores, so that those copies (HBM-bound) run beside the scoring
+// instead of after the selection.  Created on first use (non-blocking, the
+// default priority); the fork and the join are events.  The device's mutex
+// is held from the fork to the join, so calls from several host threads
+// cannot interleave their events.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream, locked through *lock.
+hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream &ss = g_side[dev];
+  *lock = std::unique_lock<std::mutex>(ss.mu);
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t ef = nullptr, ej = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ef, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (ej) hipEventDestroy(ej);
+      if (ef) hipEventDestroy(ef);
+      if (st) hipStreamDestroy(st);
+      return e;
+    }
+    ss.s = st;
+    ss.fork = ef;
+    ss.join = ej;
+  }
+  *out = &ss;
+  return hipSuccess;
 }
 
 fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, const void *v,
@@ -245,10 +305,13 @@ fkv_status_t check_compress_out(const Plan &p, const void *q, const fkv_ckv_t *o
 // Scoring, selection and compaction of one layer over the window `win`
 // (plain or rolling) with the plan p.
 // kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
+// side: copy the compaction jobs that do not depend on the scores on the
+// device's side stream, beside the scoring (not with kv_scales or ev).
 fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
                              const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
                              size_t workspace_bytes, void *stream,
-                             const float *kv_scales = nullptr, hipEvent_t *ev = nullptr) {
+                             const float *kv_scales = nullptr, hipEvent_t *ev = nullptr,
+                             bool side = false) {
   fkv_status_t st = check_compress_out(p, q, out);
   if (st != FKV_OK) return st;
   if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
@@ -261,8 +324,30 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   fkv::CopySlot *slots = reinterpret_cast<fkv::CopySlot *>(ws + p.ws_slot_off);
   const float c = log2e_scale(*desc);
 
+  const bool split = side && !kv_scales && !ev;
+  SideStream *ss = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  // Joins the side stream into the caller's stream on every return after
+  // the fork (before the lock is released); the dynamic compaction joins
+  // explicitly.
+  struct Join {
+    hipStream_t s = nullptr;
+    hipEvent_t ev = nullptr;
+    ~Join() {
+      if (ev) hipStreamWaitEvent(s, ev, 0);
+    }
+  } join;
+  if (split) {
+    // 0. fork point: the side stream starts from the caller's stream as it
+    // stands before the scoring
+    hipError_t e = side_stream(&ss, &side_lock);
+    if (e != hipSuccess) return hip_fail(e, "side stream creation");
+    e = hipEventRecord(ss->fork, s);
+    if (e != hipSuccess) return hip_fail(e, "side stream fork");
+  }
   if (ev) hipEventRecord(ev[0], s);
   // 1. dynamic-head scoring: per (sampled query, frame) log-sum-exp
+  hipError_t score_err = hipSuccess;
   if (p.n_dyn > 0) {
     fkv::ScoreArgs sa;
     sa.q = q;
@@ -280,10 +365,36 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     sa.c = c;
     std::memcpy(sa.dyn_heads, p.dyn_heads, sizeof(sa.dyn_heads));
     std::memcpy(sa.fh, p.fh, sizeof(sa.fh));
-    hipError_t e = desc->dtype == FKV_BF16 ? fkv::launch_score_bf16(sa, s)
-                                           : fkv::launch_score_f32(sa, s);
-    if (e != hipSuccess) return hip_fail(e, "scoring kernel launch");
+    score_err = desc->dtype == FKV_BF16 ? fkv::launch_score_bf16(sa, s)
+                                        : fkv::launch_score_f32(sa, s);
   }
+  if (split) {
+    // The score-independent copies on the side stream, enqueued after the
+    // scoring so that the scoring workgroups are dispatched first and the
+    // copies fill the remaining room.
+    hipError_t e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "side stream fork");
+    fkv::FixedCopyPlan cp;
+    cp.win = win;
+    cp.k_out = reinterpret_cast<char *>(out->k);
+    cp.v_out = reinterpret_cast<char *>(out->v);
+    cp.H = p.H;
+    cp.T = p.T;
+    cp.chunks = (p.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
+    std::memcpy(cp.fh, p.fh, sizeof(cp.fh));
+    std::memcpy(cp.fixed_off_h, p.fixed_off, sizeof(cp.fixed_off_h));
+    std::memcpy(cp.n_hist_fixed, p.n_hist_fixed, sizeof(cp.n_hist_fixed));
+    std::memcpy(cp.kept, p.kept, sizeof(cp.kept));
+    std::memcpy(cp.static_bits, p.static_bits, sizeof(cp.static_bits));
+    std::memcpy(cp.tok_off_h, p.tok_off, sizeof(cp.tok_off_h));
+    const hipError_t el = fkv::launch_compact_fixed(cp, ss->s);
+    e = hipEventRecord(ss->join, ss->s);
+    if (e != hipSuccess) return hip_fail(e, "side stream join");
+    join.s = s;
+    join.ev = ss->join;
+    if (el != hipSuccess) return hip_fail(el, "compaction kernel launch");
+  }
+  if (score_err != hipSuccess) return hip_fail(score_err, "scoring kernel launch");
   if (ev) hipEventRecord(ev[1], s);
   // 2. selection, offsets and compaction slots
   {
@@ -301,16 +412,22 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     sa.F_tot = p.Ft;
     sa.n_s = p.n_s;
     sa.budget = p.budget;
+    sa.dyn_slots_only = split ? 1 : 0;
     std::memcpy(sa.fh, p.fh, sizeof(sa.fh));
     std::memcpy(sa.dyn_index, p.dyn_index, sizeof(sa.dyn_index));
     std::memcpy(sa.static_bits, p.static_bits, sizeof(sa.static_bits));
     std::memcpy(sa.seg_off_h, p.seg_off, sizeof(sa.seg_off_h));
-    std::memcpy(sa.slot_off_h, p.slot_off, sizeof(sa.slot_off_h));
+    std::memcpy(sa.slot_off_h, split ? p.dyn_slot_off : p.slot_off, sizeof(sa.slot_off_h));
     std::memcpy(sa.tok_off_h, p.tok_off, sizeof(sa.tok_off_h));
     hipError_t e = fkv::launch_select(sa, s);
     if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
   }
   if (ev) hipEventRecord(ev[2], s);
+  if (join.ev) {
+    const hipError_t e = hipStreamWaitEvent(s, join.ev, 0);
+    join.ev = nullptr;
+    if (e != hipSuccess) return hip_fail(e, "side stream join");
+  }
   // 3. compaction
   if (kv_scales) {
     fkv::CompactFp8Args ca;
@@ -339,7 +456,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     ca.F_c = p.Fc;
     ca.chunks = (p.T + fkv::kCompactRows - 1) / fkv::kCompactRows;
     std::memcpy(ca.fh, p.fh, sizeof(ca.fh));
-    hipError_t e = fkv::launch_compact(ca, p.slot_off[p.H], s);
+    hipError_t e = fkv::launch_compact(ca, split ? p.dyn_slot_off[p.H] : p.slot_off[p.H], s);
     if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
   }
   if (ev) hipEventRecord(ev[3], s);
@@ -453,7 +570,7 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   if (st != FKV_OK) return st;
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
-                         workspace_bytes, stream);
+                         workspace_bytes, stream, nullptr, nullptr, true);
 }
 
 fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const void *k_cache,
@@ -596,7 +713,8 @@ fkv_status_t fkv_compress_ragged(const fkv_desc_t *desc, const void *q, const fk
   win.hist_off = hist->tok_off;
   win.cur_k = reinterpret_cast<const char *>(cur_k);
   win.cur_v = reinterpret_cast<const char *>(cur_v);
-  return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream);
+  return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
+                         nullptr, true);
 }
 
 fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, const void *cur_v,

@@ -10,18 +10,23 @@
 // thread moves 16-byte pieces, each wave reads whole 256-byte head rows from
 // the window (token-major, or a previous compressed cache for history
 // frames) and writes them contiguously; eight loads are in flight per thread
-// before the first store.  Without slots the kernel refreshes the current
-// chunk of an existing compressed cache (selection reused across the
+// before the first store.  Loads and stores carry the non-temporal hint: the
+// bytes are touched once, and the scoring running beside the copies keeps
+// re-reading its K tiles from L2.  Without slots the kernel refreshes the
+// current chunk of an existing compressed cache (selection reused across the
 // denoising steps of one chunk).
+//
+// The copies that the plan fixes before any score is known (static heads'
+// kept frames, every head's current chunk) have a kernel of their own, which
+// runs beside the scoring; the selection then writes slots for the dynamic
+// heads' kept history frames only.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
 namespace fkv {
 namespace {
 
-constexpr int kThreads = 256;
-
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+__global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   const int slot = blockIdx.x / a.chunks;
   const int c = blockIdx.x - slot * a.chunks;
   CopySlot sl;
@@ -35,49 +40,33 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     sl.src_frame = a.fh[sl.head] + j;
     sl.dst_row = a.out_tok_off[sl.head + 1] - (int64_t)(a.F_c - j) * a.T;
   }
-  const int r0 = c * kCompactRows;
-  const int nrows = min(kCompactRows, a.T - r0);
-  const int row_bytes = a.win.row_bytes;
-  const int v16 = row_bytes >> 4;          // 16-byte pieces per row
-  const int items = nrows * v16;
-  int64_t src_stride;
-  const char *ks = frame_rows(a.win, false, sl.head, a.fh[sl.head], sl.src_frame, a.T,
-                              &src_stride) + r0 * src_stride;
-  const char *vs = frame_rows(a.win, true, sl.head, a.fh[sl.head], sl.src_frame, a.T,
-                              &src_stride) + r0 * src_stride;
-  char *kd = a.k_out + (sl.dst_row + r0) * row_bytes;
-  char *vd = a.v_out + (sl.dst_row + r0) * row_bytes;
+  copy_rows(a.win, a.fh[sl.head], sl, c, a.T, a.k_out, a.v_out);
+}
 
-  constexpr int U = 4;
-  for (int base = 0; base < items; base += kThreads * U) {
-    u32x4 kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kThreads + threadIdx.x;
-      if (idx < items) {
-        const int r = idx / v16, p = idx - r * v16;
-        const int64_t so = r * src_stride + p * 16;
-        kr[u] = ld16(ks + so);
-        vr[u] = ld16(vs + so);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kThreads + threadIdx.x;
-      if (idx < items) {
-        st16(kd + (int64_t)idx * 16, kr[u]);
-        st16(vd + (int64_t)idx * 16, vr[u]);
-      }
-    }
-  }
+// The compaction jobs fixed by the plan alone (static heads' kept frames,
+// every head's current chunk): workgroup b copies chunk b % chunks of job
+// b / chunks.  Independent of the scores, so it may run beside them.
+__global__ __launch_bounds__(256) void compact_fixed_kernel(FixedCopyPlan p) {
+  const int job = blockIdx.x / p.chunks;
+  const int c = blockIdx.x - job * p.chunks;
+  const CopySlot sl = fixed_slot(p, job);
+  copy_rows(p.win, p.fh[sl.head], sl, c, p.T, p.k_out, p.v_out);
 }
 
 }  // namespace
 
+hipError_t launch_compact_fixed(const FixedCopyPlan &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.fixed_off_h[p.H] * p.chunks;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_fixed_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs &a, int total_slots, hipStream_t s) {
   if (total_slots <= 0) return hipSuccess;
   dim3 grid((unsigned)total_slots * (unsigned)a.chunks);
-  hipLaunchKernelGGL(compact_kernel, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

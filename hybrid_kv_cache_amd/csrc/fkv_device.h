@@ -191,6 +191,14 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// Streaming forms (non-temporal hint): data touched once, kept from
+// displacing lines that other workgroups re-read from L2.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st16_stream(void *p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
 
 // First byte of the T-row frame f of head h's window (fh_h history frames,
 // then the current chunk; see WinView), and the bytes between its rows.
@@ -208,6 +216,75 @@ __device__ __forceinline__ const char *frame_rows(const WinView &w, bool want_v,
   const char *base = want_v ? w.cur_v : w.cur_k;
   *row_stride = w.tm_row_bytes;
   return base + (int64_t)(f - fh_h) * T * w.tm_row_bytes + (int64_t)h * w.row_bytes;
+}
+
+// Copy of rows [64 c, 64 c + 64) (clipped to T) of one compaction job: the
+// K and V rows of window frame sl.src_frame of head sl.head go to compacted
+// rows sl.dst_row + 64 c ... of k_out / v_out.  256 threads, 16-byte pieces,
+// eight loads in flight per thread before the stores.
+__device__ __forceinline__ void copy_rows(const WinView &win, int fh_h, CopySlot sl, int c,
+                                          int T, char *k_out, char *v_out) {
+  constexpr int kThreads = 256;
+  const int r0 = c * kCompactRows;
+  const int nrows = min(kCompactRows, T - r0);
+  const int row_bytes = win.row_bytes;
+  const int v16 = row_bytes >> 4;          // 16-byte pieces per row
+  const int items = nrows * v16;
+  int64_t src_stride;
+  const char *ks = frame_rows(win, false, sl.head, fh_h, sl.src_frame, T, &src_stride) +
+                   r0 * src_stride;
+  const char *vs = frame_rows(win, true, sl.head, fh_h, sl.src_frame, T, &src_stride) +
+                   r0 * src_stride;
+  char *kd = k_out + (sl.dst_row + r0) * row_bytes;
+  char *vd = v_out + (sl.dst_row + r0) * row_bytes;
+  constexpr int U = 4;
+  for (int base = 0; base < items; base += kThreads * U) {
+    u32x4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * kThreads + threadIdx.x;
+      if (idx < items) {
+        const int r = idx / v16, p = idx - r * v16;
+        const int64_t so = r * src_stride + p * 16;
+        kr[u] = ld16_stream(ks + so);
+        vr[u] = ld16_stream(vs + so);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * kThreads + threadIdx.x;
+      if (idx < items) {
+        st16_stream(kd + (int64_t)idx * 16, kr[u]);
+        st16_stream(vd + (int64_t)idx * 16, vr[u]);
+      }
+    }
+  }
+}
+
+// The data-independent compaction job s (0 <= s < p.fixed_off_h[H]): the
+// kept history frames of static heads and the current-chunk frames of every
+// head, which the host plan fixes before any score is known.  Head h owns
+// jobs [fixed_off_h[h], fixed_off_h[h+1]): first its n_hist_fixed[h] kept
+// history frames (the set bits of static_bits[h], ascending; 0 for dynamic
+// heads), then its F_c current frames, which follow the head's kept[h]
+// history frames in its compacted range.
+__device__ __forceinline__ CopySlot fixed_slot(const FixedCopyPlan &p, int s) {
+  int h = 0;
+  while (h + 1 < p.H && p.fixed_off_h[h + 1] <= s) ++h;
+  const int j = s - p.fixed_off_h[h];
+  CopySlot sl;
+  sl.head = h;
+  if (j < p.n_hist_fixed[h]) {
+    uint64_t b = p.static_bits[h];
+    for (int i = 0; i < j; ++i) b &= b - 1ull;
+    sl.src_frame = __ffsll((long long)b) - 1;
+    sl.dst_row = p.tok_off_h[h] + (int64_t)j * p.T;
+  } else {
+    const int cf = j - p.n_hist_fixed[h];
+    sl.src_frame = p.fh[h] + cf;
+    sl.dst_row = p.tok_off_h[h] + (int64_t)(p.kept[h] + cf) * p.T;
+  }
+  return sl;
 }
 
 }  // namespace fkv

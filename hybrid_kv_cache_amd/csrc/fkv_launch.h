@@ -61,6 +61,8 @@ struct SelectArgs {
   float *seg_score;     // [H * F_h] or null
   CopySlot *slots;      // [total_slots]
   int32_t H, T, F_h, F_c, F_tot, n_s, budget;  // F_h: row length of seg_score
+  int32_t dyn_slots_only;  // 1: jobs only for dynamic heads' kept history frames
+                           // (the others ran with the scoring), at slot_off_h
   int32_t fh[kMaxHeads];            // history frames of each head
   int32_t dyn_index[kMaxHeads];     // -1 static, else row block in lse
   uint64_t static_bits[kMaxHeads];  // kept history frames of static heads
@@ -112,6 +114,21 @@ struct CompactArgs {
 };
 constexpr int kCompactRows = 64;
 
+// The compaction jobs that do not depend on the scores (see fixed_slot in
+// fkv_device.h): one workgroup per (job, kCompactRows-row chunk).
+struct FixedCopyPlan {
+  WinView win;
+  char *k_out;          // [rows, D]
+  char *v_out;
+  int32_t H, T, chunks;           // chunks: ceil(T / kCompactRows)
+  int32_t fh[kMaxHeads];
+  int32_t fixed_off_h[kMaxHeads + 1];
+  int32_t n_hist_fixed[kMaxHeads];
+  int32_t kept[kMaxHeads];        // kept history frames of each head
+  uint64_t static_bits[kMaxHeads];
+  int64_t tok_off_h[kMaxHeads + 1];
+};
+
 struct AttendArgs {
   const void *q;          // [Nq, H, D]
   const void *k;          // ragged [rows, D] or window [N_win, H, D]
@@ -132,6 +149,7 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 hipError_t launch_profile(const ProfileArgs &a, hipStream_t s);
 hipError_t launch_tokens(const TokenArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int total_slots, hipStream_t s);
+hipError_t launch_compact_fixed(const FixedCopyPlan &p, hipStream_t s);
 // Bytes of partial-result buffer that the balanced bf16 attention schedule
 // needs on the current device (2 slots per workgroup, 2 workgroups per CU).
 size_t attend_part_bytes();

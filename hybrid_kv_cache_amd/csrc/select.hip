@@ -209,9 +209,11 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
     const int pos = __popcll(bits & ((1ull << tid) - 1ull));
     a.seg_idx[a.seg_off_h[h] + pos] = tid;
   }
-  // Compaction slots: kept history frames (ascending), then the current chunk.
+  // Compaction slots: kept history frames (ascending), then the current chunk
+  // -- or, when the jobs that do not depend on the scores ran beside the
+  // scoring, only a dynamic head's kept history frames.
   const int kept = __popcll(bits);
-  const int nslots = kept + a.F_c;
+  const int nslots = !a.dyn_slots_only ? kept + a.F_c : (di >= 0 ? kept : 0);
   if (tid < nslots) {
     int src;
     if (tid < kept) {
