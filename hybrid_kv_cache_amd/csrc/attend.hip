@@ -80,6 +80,26 @@ __device__ __forceinline__ XcdSplit xcd_split(int pairs, int nb, int x) {
   s.k = s.ne > 0 ? (s.np + s.ne - 1) / s.ne : 0;
   return s;
 }
+// Rounds schedule on XCD x (more pairs than resident workgroups): the XCD's
+// pairs are [p_lo, p_lo + np) and slots_x workgroups of it run at a time.
+// The first w pairs run whole, one workgroup each, in full rounds plus part
+// of the last; the s pairs after them are cut in two halves (tiles
+// [0, nt/2) and [nt/2, nt)) so that the last round is full too: with
+// rem = np mod slots_x, s = rem when 2 rem <= slots_x (the last round is
+// halves only), else s = slots_x - rem (rem - s whole pairs and 2 s halves).
+struct XcdRounds {
+  int p_lo, np, w, s;
+};
+__host__ __device__ __forceinline__ XcdRounds xcd_rounds(int pairs, int slots_x, int x) {
+  XcdRounds r;
+  r.p_lo = pairs * x / 8;
+  r.np = pairs * (x + 1) / 8 - r.p_lo;
+  const int rem = r.np % slots_x;
+  r.s = rem == 0 ? 0 : (2 * rem <= slots_x ? rem : slots_x - rem);
+  r.w = r.np - r.s;
+  return r;
+}
+
 // First tail tile of a pair with nt tiles (nt when nothing is cut).  A
 // tail workgroup runs its k tails one after the other, each restarting the
 // copy pipeline, and takes about 9/8 the time per tile of a main workgroup;
@@ -114,11 +134,28 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   //  - With one (fewer pairs than workgroups, all resident): the split
   //    schedule of xcd_split; a pair cut into a main part and a tail leaves
   //    two partial results for the combine kernel.
+  //  - With one and more pairs than resident workgroups: the rounds
+  //    schedule of xcd_rounds; its halved pairs leave two partial results
+  //    in slots 2 (x cut_max + c) and 2 (x cut_max + c) + 1.
   const int nb = gridDim.x, x = blockIdx.x & 7, xs = blockIdx.x >> 3;
-  int p0, n_items, k = 0, tail = 0;
+  int p0, n_items, k = 0, tail = 0, slot0 = -1;
   if (!a.part) {
     p0 = x * (nb >> 3) + min(x, nb & 7) + xs;
     n_items = 1;
+  } else if (a.sched == 2) {
+    const XcdRounds xr = xcd_rounds(pairs, a.slots_x, x);
+    n_items = 1;
+    if (xs < xr.w) {
+      p0 = xr.p_lo + xs;
+    } else if (xs < xr.w + 2 * xr.s) {
+      const int c = (xs - xr.w) >> 1;
+      tail = (xs - xr.w) & 1;
+      p0 = xr.p_lo + xr.w + c;
+      k = -1;  // halves
+      slot0 = 2 * (x * a.cut_max + c);
+    } else {
+      return;  // padding: XCDs with fewer pairs
+    }
   } else {
     const XcdSplit sp = xcd_split(pairs, nb, x);
     k = sp.k;
@@ -178,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   const int p = p0 + item;
   const int h = p / ntq, qt = p - h * ntq;
   const int nt = head_tiles(a, h);
-  const int ts = split_tile(nt, k);
+  const int ts = k < 0 ? nt / 2 : split_tile(nt, k);
   const int t0 = tail ? ts : 0, t1 = tail ? nt : ts;
   if (t0 >= t1) continue;
   const int qi = qt * kBM + wave * 32 + col;
@@ -370,8 +407,9 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     }
   } else {
     // Part of a pair: partial results into slot 2 p (main part) or
-    // 2 p + 1 (tail).
-    float *slot = a.part + (int64_t)(2 * p + tail) * kPartFloats;
+    // 2 p + 1 (tail); for a halved pair of the rounds schedule, slot0 or
+    // slot0 + 1.
+    float *slot = a.part + (int64_t)((slot0 >= 0 ? slot0 : 2 * p) + tail) * kPartFloats;
     const int ql = wave * 32 + col;
     const float lt = pair_sum(l);
 #pragma unroll
@@ -397,20 +435,34 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
 // Merge of the two halves of every cut pair (block p: pair p):
 // O = sum_s O_s 2^(m_s - M), l = sum_s l_s 2^(m_s - M), M = max_s m_s,
 // out = O / l.  Thread t: query t / 2 of the tile, dims 64 (t & 1) .. +63.
+// Split schedule: block p merges pair p.  Rounds schedule: block b merges
+// the halved pair c = b / 8 of XCD x = b % 8 (if there is one).
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
-  const int p = blockIdx.x;
   const int ntq = (a.n_q + kBM - 1) / kBM;
   const int pairs = ntq * a.H;
-  int x = 0;
-  while (x < 7 && p >= pairs * (x + 1) / 8) ++x;
-  const XcdSplit sp = xcd_split(pairs, a.n_wg, x);
+  int p, nt, ts, slot;
+  if (a.sched == 2) {
+    const int x = blockIdx.x & 7, c = blockIdx.x >> 3;
+    const XcdRounds xr = xcd_rounds(pairs, a.slots_x, x);
+    if (c >= xr.s) return;
+    p = xr.p_lo + xr.w + c;
+    nt = head_tiles(a, p / ntq);
+    ts = nt / 2;
+    slot = 2 * (x * a.cut_max + c);
+  } else {
+    p = blockIdx.x;
+    int x = 0;
+    while (x < 7 && p >= pairs * (x + 1) / 8) ++x;
+    const XcdSplit sp = xcd_split(pairs, a.n_wg, x);
+    nt = head_tiles(a, p / ntq);
+    ts = split_tile(nt, sp.k);
+    slot = 2 * p;
+  }
   const int h = p / ntq, qt = p - h * ntq;
-  const int nt = head_tiles(a, h);
-  const int ts = split_tile(nt, sp.k);
   if (ts == 0 || ts == nt) return;  // written whole by one workgroup
 
   const int t = threadIdx.x, ql = t >> 1, d0 = (t & 1) * 64;
-  const float *s0 = a.part + (int64_t)(2 * p) * kPartFloats;
+  const float *s0 = a.part + (int64_t)slot * kPartFloats;
   const float *s1 = s0 + kPartFloats;
   const float m0 = s0[kBM * kD + ql], m1 = s1[kBM * kD + ql];
   const float M = fmaxf(m0, m1);
@@ -559,16 +611,42 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
   // Two workgroups fit on a CU (64 KiB of LDS each).  The split schedule
   // runs exactly that many, all resident at once, when there is at most one
   // pair per CU; otherwise whole pairs are dealt out as workgroups finish.
+  // With more pairs than resident workgroups, whole pairs are dealt out in
+  // rounds and the remainder halved so that the last round is full too
+  // (xcd_rounds); the halves need 2 slots each, at most nb / 2 of them.
   const int nb = 2 * device_cus();
   a.part = nullptr;
   a.n_wg = pairs;
-  if (part && nb > 0 && nb % 8 == 0 && 2 * pairs <= nb &&
-      part_bytes >= (size_t)2 * nb * kPartFloats * sizeof(float)) {
+  a.sched = 0;
+  a.slots_x = 0;
+  a.cut_max = 0;
+  int combine_blocks = 0;
+  const bool have_part = part && nb > 0 && nb % 8 == 0 &&
+                         part_bytes >= (size_t)2 * nb * kPartFloats * sizeof(float);
+  if (have_part && 2 * pairs <= nb) {
     a.part = static_cast<float *>(part);
     a.n_wg = nb;
+    a.sched = 1;
+    combine_blocks = pairs;
+  } else if (have_part && pairs > nb) {
+    int cut_max = 0, per_x = 0;
+    for (int x = 0; x < 8; ++x) {
+      const XcdRounds xr = xcd_rounds(pairs, nb / 8, x);
+      cut_max = xr.s > cut_max ? xr.s : cut_max;
+      per_x = xr.w + 2 * xr.s > per_x ? xr.w + 2 * xr.s : per_x;
+    }
+    if (cut_max > 0) {
+      a.part = static_cast<float *>(part);
+      a.n_wg = 8 * per_x;
+      a.sched = 2;
+      a.slots_x = nb / 8;
+      a.cut_max = cut_max;
+      combine_blocks = 8 * cut_max;
+    }
   }
   hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
-  if (a.part) hipLaunchKernelGGL(attend_combine_kernel, dim3(pairs), dim3(256), 0, s, a);
+  if (combine_blocks > 0)
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(combine_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

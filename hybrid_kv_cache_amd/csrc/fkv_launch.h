@@ -139,8 +139,11 @@ struct AttendArgs {
   int32_t dense_len;      // window length when tok_off is null
   int32_t n_q, H, D;
   float c;                // scale * log2(e)
-  float *part;            // partial-result slots (balanced bf16 schedule) or null
-  int32_t n_wg;           // workgroups of the balanced schedule
+  float *part;            // partial-result slots (balanced bf16 schedules) or null
+  int32_t n_wg;           // workgroups of the balanced schedules
+  int32_t sched;          // 0: one workgroup per pair; 1: split; 2: rounds + halves
+  int32_t slots_x;        // schedule 2: resident workgroups per XCD
+  int32_t cut_max;        // schedule 2: most halved pairs on one XCD
 };
 
 hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s);
