@@ -243,8 +243,12 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
     hipStream_t st = nullptr;
     hipEvent_t ef = nullptr, ej = nullptr;
     e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ef, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, hipEventDisableTiming);
+    // The events order two streams of one device and are never waited on by
+    // the host: no timing, and no system-scope fence (the kernels' own
+    // device-scope release and acquire make their writes visible).
+    const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ef, flags);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, flags);
     if (e != hipSuccess) {
       if (ej) hipEventDestroy(ej);
       if (ef) hipEventDestroy(ef);
