@@ -12,9 +12,10 @@
 // F_h for every head of a plain window; a rolling cache gives each head its
 // own history length.)
 //
-// One workgroup (4 waves) per head.  Dynamic heads: one sampled query per
+// One workgroup per head (16 waves; 4 when the window has more than 24
+// frames).  Dynamic heads: one sampled query per
 // thread at a time, the softmax over its frames in registers, masses summed
-// per thread, then over each wave and over the 4 waves in a fixed order
+// per thread, then over each wave and over the waves in a fixed order
 // (deterministic).
 // Wave 0 then sorts the (score, frame) pairs with a 64-lane bitonic network
 // (lane exchanges by DPP and permlane swaps, not the LDS crossbar) and marks
@@ -83,9 +84,14 @@ __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib)
   return sa > sb || (sa == sb && ia < ib);
 }
 
+// Waves of the profiling workgroup, and of the selection workgroup when a
+// head's window has more than 24 frames; up to 24 frames the selection uses
+// 16 waves, so that one pass over the sampled queries covers up to 1024 of
+// them (each pass waits for its loads once).
 constexpr int kSelWaves = 4;
+constexpr int kSelWavesWide = 16;
 
-// Masses of one dynamic head: thread t takes sampled queries t, t + 256, ...;
+// Masses of one dynamic head: thread t takes sampled queries t, t + 64 W, ...;
 // for each, the ft frame log-sum-exps (base 2; frame f at base[f * n_s + r],
 // so that a wave reads each frame with one coalesced load) become a softmax
 // over the head's window, whose first fh entries (the history) are added to
@@ -93,14 +99,14 @@ constexpr int kSelWaves = 4;
 // in part[w][f].
 constexpr int kPartFrames = kMaxHistFrames + kMaxCurFrames;
 
-template <int FT>
+template <int FT, int W>
 __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int ft,
                                                   int fh, float (*part)[kPartFrames], int tid,
                                                   int lane, int wave) {
   float acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = 0.f;
-  for (int r = tid; r < n_s; r += 64 * kSelWaves) {
+  for (int r = tid; r < n_s; r += 64 * W) {
     float v[FT];
 #pragma unroll
     for (int f = 0; f < FT; ++f) v[f] = f < ft ? base[(int64_t)f * n_s + r] : -INFINITY;
@@ -126,8 +132,9 @@ __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, in
   }
 }
 
-__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
-  __shared__ float part[kSelWaves][kPartFrames];
+template <int W>
+__global__ __launch_bounds__(64 * W) void select_kernel(SelectArgs a) {
+  __shared__ float part[W][kPartFrames];
   __shared__ unsigned long long kept_bits_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
@@ -152,17 +159,17 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelectArgs a) {
     // reduction over threads (deterministic).
     const float *base = a.lse + (int64_t)di * a.n_s * a.F_tot;
     const int ft = fh + a.F_c;
-    if (ft <= 24)
-      accumulate_masses<24>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
+    if (W == kSelWavesWide)
+      accumulate_masses<24, W>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
     else
-      accumulate_masses<72>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
+      accumulate_masses<72, W>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
     __syncthreads();
     if (wave == 0) {
       float score = -INFINITY;
       if (lane < fh) {
         float sum = part[0][lane];
 #pragma unroll
-        for (int w = 1; w < kSelWaves; ++w) sum += part[w][lane];
+        for (int w = 1; w < W; ++w) sum += part[w][lane];
         score = sum / (float)a.n_s;
         if (a.seg_score) a.seg_score[(int64_t)h * a.F_h + lane] = score;
       } else if (a.seg_score && lane < a.F_h) {
@@ -241,9 +248,11 @@ __global__ __launch_bounds__(64 * kSelWaves) void profile_kernel(ProfileArgs a) 
   const int h = blockIdx.x;
   const float *base = a.lse + (int64_t)h * a.n_s * a.F_tot;
   if (a.F_tot <= 24)
-    accumulate_masses<24>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane, wave);
+    accumulate_masses<24, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane,
+                                     wave);
   else
-    accumulate_masses<72>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane, wave);
+    accumulate_masses<72, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane,
+                                     wave);
   __syncthreads();
   if (tid < a.F_tot) {
     float sum = part[0][tid];
@@ -261,7 +270,10 @@ hipError_t launch_profile(const ProfileArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.H), dim3(64 * kSelWaves), 0, s, a);
+  if (a.F_tot <= 24)
+    hipLaunchKernelGGL(select_kernel<kSelWavesWide>, dim3(a.H), dim3(64 * kSelWavesWide), 0, s, a);
+  else
+    hipLaunchKernelGGL(select_kernel<kSelWaves>, dim3(a.H), dim3(64 * kSelWaves), 0, s, a);
   return hipGetLastError();
 }
 
