@@ -133,6 +133,12 @@ def measure(wname, args, fkv, torch, W):
         time_loop(fn, layers, args.steps, args.warmup, torch)
         return None
     ms_step = time_loop(step, layers, args.steps, args.warmup, torch)
+    # the same layer pass as one call (fkv_compress_attend: attention without
+    # a workspace, the unscored heads attending beside the scoring)
+    ms_step_one_call = time_loop(
+        lambda L: fkv.fkv_compress_attend(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m,
+                                          L.ckv, L.out),
+        layers, args.steps, args.warmup, torch)
     ms_compress = time_loop(lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
                                                        w.budget_m, L.ckv),
                             layers, args.steps, args.warmup, torch)
@@ -153,7 +159,8 @@ def measure(wname, args, fkv, torch, W):
     attn_flop = 4.0 * w.n_q * D * kept
     dense_flop = 4.0 * w.n_q * D * w.n_win * w.num_heads
     elt = 2 if w.dtype == "bf16" else 4
-    return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_compress=ms_compress,
+    return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_step_one_call=ms_step_one_call,
+                ms_compress=ms_compress,
                 stage_ms=stage_ms,
                 ms_attend=ms_attend, ms_dense=ms_dense, attn_flop=attn_flop,
                 dense_flop=dense_flop, n_layers=len(layers),
@@ -524,7 +531,8 @@ def main():
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": attn_tflops / peak, "traffic": traffic_record("attend", w.name)},
         "breakdown_ms": {"compress": r["ms_compress"], "attend": r["ms_attend"],
-                         "attend_dense": r["ms_dense"]},
+                         "attend_dense": r["ms_dense"],
+                         "step_one_call": r["ms_step_one_call"]},
         "speedup_vs_full_kv": r["ms_dense"] / r["ms_step"],
         "attention_speedup_vs_full_kv": r["ms_dense"] / r["ms_attend"],
         "kept_fraction_of_history_kv": r["kept_frac_hist"],
@@ -538,7 +546,8 @@ def main():
             "workload": w2.name, "value": w2.n_q / (r2["ms_step"] * 1e-3),
             "unit": "query tok/s per layer", "ms_per_step": r2["ms_step"],
             "breakdown_ms": {"compress": r2["ms_compress"], "attend": r2["ms_attend"],
-                             "attend_dense": r2["ms_dense"]},
+                             "attend_dense": r2["ms_dense"],
+                             "step_one_call": r2["ms_step_one_call"]},
             "attend_tflops": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12,
             "attend_frac_of_peak": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12 / peak,
             "speedup_vs_full_kv": r2["ms_dense"] / r2["ms_step"],

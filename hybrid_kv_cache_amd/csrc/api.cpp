@@ -227,6 +227,7 @@ struct SideStream {
   std::mutex mu;
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t copied = nullptr;  // after the fixed copies (fkv_compress_attend)
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
@@ -241,7 +242,7 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
   *lock = std::unique_lock<std::mutex>(ss.mu);
   if (!ss.s) {
     hipStream_t st = nullptr;
-    hipEvent_t ef = nullptr, ej = nullptr;
+    hipEvent_t ef = nullptr, ej = nullptr, ec = nullptr;
     e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
     // The events order two streams of one device and are never waited on by
     // the host: no timing, and no system-scope fence (the kernels' own
@@ -249,7 +250,9 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
     const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ef, flags);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, flags);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ec, flags);
     if (e != hipSuccess) {
+      if (ec) hipEventDestroy(ec);
       if (ej) hipEventDestroy(ej);
       if (ef) hipEventDestroy(ef);
       if (st) hipStreamDestroy(st);
@@ -258,6 +261,7 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
     ss.s = st;
     ss.fork = ef;
     ss.join = ej;
+    ss.copied = ec;
   }
   *out = &ss;
   return hipSuccess;
@@ -288,6 +292,7 @@ fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, co
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   a.part = nullptr;
   a.n_wg = 0;
+  a.n_sel = 0;
   hipError_t e = d->dtype == FKV_BF16 ? fkv::launch_attend_bf16(a, workspace, workspace_bytes, s)
                                       : fkv::launch_attend_f32(a, s);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -306,16 +311,47 @@ fkv_status_t check_compress_out(const Plan &p, const void *q, const fkv_ckv_t *o
   return FKV_OK;
 }
 
+// Attention over the ragged cache `out` of the heads that have scored frames
+// (scored = true) or of the others, with the plan's row offsets.
+hipError_t attend_heads(const fkv_desc_t *d, const Plan &p, const void *q, const fkv_ckv_t *out,
+                        void *attend_out, bool scored, hipStream_t s) {
+  fkv::AttendArgs a;
+  a.q = q;
+  a.k = out->k;
+  a.v = out->v;
+  a.out = attend_out;
+  a.tok_off = nullptr;
+  a.kv_row_stride = d->head_dim;
+  a.dense_len = 0;
+  a.n_q = p.n_q;
+  a.H = p.H;
+  a.D = p.D;
+  a.c = log2e_scale(*d);
+  a.part = nullptr;
+  a.n_wg = 0;
+  a.n_sel = 0;
+  for (int h = 0; h < p.H; ++h)
+    if ((p.dyn_index[h] >= 0) == scored) a.sel[a.n_sel++] = h;
+  for (int h = a.n_sel; h < fkv::kMaxHeads; ++h) a.sel[h] = 0;
+  std::memcpy(a.host_off, p.tok_off, sizeof(a.host_off));
+  if (a.n_sel == 0) return hipSuccess;
+  return fkv::launch_attend_bf16_heads(a, s);
+}
+
 // Scoring, selection and compaction of one layer over the window `win`
 // (plain or rolling) with the plan p.
 // kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
 // side: copy the compaction jobs that do not depend on the scores on the
 // device's side stream, beside the scoring (not with kv_scales or ev).
+// attend_out (bf16, with side): also the attention of the compressed cache
+// into attend_out [Nq, H, D], one workgroup per (head, 128-query tile): the
+// heads whose copies are all fixed by the plan right after those copies on
+// the side stream, the others after their copies on the caller's stream.
 fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *q,
                              const fkv::WinView &win, const fkv_ckv_t *out, void *workspace,
                              size_t workspace_bytes, void *stream,
                              const float *kv_scales = nullptr, hipEvent_t *ev = nullptr,
-                             bool side = false) {
+                             bool side = false, void *attend_out = nullptr) {
   fkv_status_t st = check_compress_out(p, q, out);
   if (st != FKV_OK) return st;
   if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
@@ -391,12 +427,19 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     std::memcpy(cp.kept, p.kept, sizeof(cp.kept));
     std::memcpy(cp.static_bits, p.static_bits, sizeof(cp.static_bits));
     std::memcpy(cp.tok_off_h, p.tok_off, sizeof(cp.tok_off_h));
-    const hipError_t el = fkv::launch_compact_fixed(cp, ss->s);
+    hipError_t el = fkv::launch_compact_fixed(cp, ss->s);
+    if (attend_out && el == hipSuccess) {
+      // The heads with no scored frames are complete once the fixed copies
+      // are: their attention starts here, beside the scoring and selection.
+      e = hipEventRecord(ss->copied, ss->s);
+      if (e != hipSuccess) el = e;
+      if (el == hipSuccess) el = attend_heads(desc, p, q, out, attend_out, false, ss->s);
+    }
     e = hipEventRecord(ss->join, ss->s);
     if (e != hipSuccess) return hip_fail(e, "side stream join");
     join.s = s;
     join.ev = ss->join;
-    if (el != hipSuccess) return hip_fail(el, "compaction kernel launch");
+    if (el != hipSuccess) return hip_fail(el, "side stream launch");
   }
   if (score_err != hipSuccess) return hip_fail(score_err, "scoring kernel launch");
   if (ev) hipEventRecord(ev[1], s);
@@ -427,7 +470,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
   }
   if (ev) hipEventRecord(ev[2], s);
-  if (join.ev) {
+  if (join.ev && !attend_out) {
     const hipError_t e = hipStreamWaitEvent(s, join.ev, 0);
     join.ev = nullptr;
     if (e != hipSuccess) return hip_fail(e, "side stream join");
@@ -464,6 +507,13 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
   }
   if (ev) hipEventRecord(ev[3], s);
+  if (attend_out && split) {
+    // 4. attention of the scored heads, whose current chunk the side stream
+    // copied (the side stream's own attention is joined on return)
+    hipError_t e = hipStreamWaitEvent(s, ss->copied, 0);
+    if (e == hipSuccess) e = attend_heads(desc, p, q, out, attend_out, true, s);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  }
   return ok();
 }
 
@@ -575,6 +625,27 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
                          workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+fkv_status_t fkv_compress_attend(const fkv_desc_t *desc, const void *q, const void *k_cache,
+                                 const void *v_cache, const uint8_t *head_role,
+                                 const uint8_t *static_keep_mask, int32_t budget_m,
+                                 const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
+                                 void *attend_out, void *stream) {
+  Plan p;
+  fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
+  if (st != FKV_OK) return st;
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  if (!attend_out) return fail(FKV_ERR_NULL, "attend_out is NULL");
+  const fkv::WinView win = plain_window(desc, k_cache, v_cache);
+  if (desc->dtype == FKV_BF16)
+    return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
+                           nullptr, true, attend_out);
+  // fp32: the compression, then the attention of every head
+  st = compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
+                       nullptr, true);
+  if (st != FKV_OK) return st;
+  return attend_common(desc, q, out->k, out->v, out->tok_off, attend_out, nullptr, 0, stream);
 }
 
 fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const void *k_cache,

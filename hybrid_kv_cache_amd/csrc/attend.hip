@@ -44,8 +44,9 @@ struct KvView {
 
 __device__ __forceinline__ KvView kv_view(const AttendArgs &a, int h) {
   KvView r;
-  if (a.tok_off) {
-    const int64_t lo = a.tok_off[h], hi = a.tok_off[h + 1];
+  if (a.n_sel > 0 || a.tok_off) {
+    const int64_t lo = a.n_sel > 0 ? a.host_off[h] : a.tok_off[h];
+    const int64_t hi = a.n_sel > 0 ? a.host_off[h + 1] : a.tok_off[h + 1];
     r.k = reinterpret_cast<const __bf16 *>(a.k) + lo * kD;
     r.v = reinterpret_cast<const __bf16 *>(a.v) + lo * kD;
     r.rs = kD;
@@ -60,7 +61,9 @@ __device__ __forceinline__ KvView kv_view(const AttendArgs &a, int h) {
 }
 
 __device__ __forceinline__ int head_tiles(const AttendArgs &a, int h) {
-  const int64_t len = a.tok_off ? a.tok_off[h + 1] - a.tok_off[h] : (int64_t)a.dense_len;
+  const int64_t len = a.n_sel > 0 ? a.host_off[h + 1] - a.host_off[h]
+                      : a.tok_off ? a.tok_off[h + 1] - a.tok_off[h]
+                                  : (int64_t)a.dense_len;
   return (int)((len + kKT - 1) / kKT);
 }
 
@@ -124,8 +127,9 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   const int col = lane & 31, g = lane >> 5;
   const float c = a.c;
   const int ntq = (a.n_q + kBM - 1) / kBM;
-  const int pairs = ntq * a.H;
-  // Work: (head, 128-query tile) pairs, p = h * ntq + qt, pair p holding the
+  const int pairs = ntq * (a.n_sel > 0 ? a.n_sel : a.H);
+  // Work: (head, 128-query tile) pairs, p = h * ntq + qt (h the position in
+  // sel for a head subset), pair p holding the
   // tiles(h) key tiles of its head.  Workgroups are handed to the 8 XCDs
   // round-robin (workgroup b runs on XCD b % 8); each XCD takes a contiguous
   // run of pairs, so the workgroups sharing an L2 stream the same head's K/V
@@ -213,7 +217,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
 
   for (int item = 0; item < n_items; ++item) {
   const int p = p0 + item;
-  const int h = p / ntq, qt = p - h * ntq;
+  const int hs = p / ntq, qt = p - hs * ntq;
+  const int h = a.n_sel > 0 ? __builtin_amdgcn_readfirstlane(a.sel[hs]) : hs;
   const int nt = head_tiles(a, h);
   const int ts = k < 0 ? nt / 2 : split_tile(nt, k);
   const int t0 = tail ? ts : 0, t1 = tail ? nt : ts;
@@ -647,6 +652,16 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
   hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
   if (combine_blocks > 0)
     hipLaunchKernelGGL(attend_combine_kernel, dim3(combine_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_bf16_heads(const AttendArgs &a0, hipStream_t s) {
+  if (a0.D != kD || a0.n_sel <= 0 || a0.n_sel > kMaxHeads) return hipErrorInvalidValue;
+  AttendArgs a = a0;
+  a.part = nullptr;
+  a.sched = 0;
+  a.n_wg = ((a.n_q + kBM - 1) / kBM) * a.n_sel;
+  hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

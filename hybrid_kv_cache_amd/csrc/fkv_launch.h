@@ -144,6 +144,12 @@ struct AttendArgs {
   int32_t sched;          // 0: one workgroup per pair; 1: split; 2: rounds + halves
   int32_t slots_x;        // schedule 2: resident workgroups per XCD
   int32_t cut_max;        // schedule 2: most halved pairs on one XCD
+  // Head subset (one workgroup per pair only): n_sel > 0 runs the heads
+  // sel[0 .. n_sel) alone, with their row ranges [host_off[h], host_off[h+1])
+  // of the ragged cache taken from these values instead of tok_off.
+  int32_t n_sel;
+  int32_t sel[kMaxHeads];
+  int64_t host_off[kMaxHeads + 1];
 };
 
 hipError_t launch_score_bf16(const ScoreArgs &a, hipStream_t s);
@@ -158,6 +164,8 @@ hipError_t launch_compact_fixed(const FixedCopyPlan &p, hipStream_t s);
 size_t attend_part_bytes();
 // part / part_bytes: null / 0 for one workgroup per (head, query tile).
 hipError_t launch_attend_bf16(const AttendArgs &a, void *part, size_t part_bytes, hipStream_t s);
+// The heads a.sel[0 .. a.n_sel) of the ragged cache, one workgroup per pair.
+hipError_t launch_attend_bf16_heads(const AttendArgs &a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s);
 
 // Library-owned scratch array of fkv_compress_noalloc (scratch.hip): its size

@@ -27,7 +27,8 @@ FKV_OK, FKV_ERR_NULL, FKV_ERR_SHAPE, FKV_ERR_DTYPE, FKV_ERR_BUDGET, \
 FKV_BF16, FKV_F32 = 0, 1
 FKV_STATIC, FKV_DYNAMIC = 0, 1
 
-EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_noalloc", "fkv_compress_timed",
+EXPORTED = ("fkv_plan", "fkv_compress", "fkv_compress_attend", "fkv_compress_noalloc",
+            "fkv_compress_timed",
             "fkv_plan_ragged", "fkv_compress_ragged", "fkv_refresh_current",
             "fkv_roll_static_mask",
             "fkv_plan_tokens", "fkv_compress_tokens",
@@ -78,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(SZ)]
     lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                  ctypes.POINTER(FkvCkv), P, SZ, P]
+    lib.fkv_compress_attend.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
+                                        ctypes.POINTER(FkvCkv), P, SZ, P, P]
     lib.fkv_compress_noalloc.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                          ctypes.POINTER(FkvCkv), P]
     lib.fkv_compress_timed.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
@@ -101,8 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_attend_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_attend.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_attend_dense.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, SZ, P]
-    for name in ("fkv_plan", "fkv_compress", "fkv_compress_noalloc", "fkv_compress_timed",
-                 "fkv_plan_ragged",
+    for name in ("fkv_plan", "fkv_compress", "fkv_compress_attend", "fkv_compress_noalloc",
+                 "fkv_compress_timed", "fkv_plan_ragged",
                  "fkv_compress_ragged",
                  "fkv_refresh_current", "fkv_roll_static_mask", "fkv_plan_tokens",
                  "fkv_compress_tokens", "fkv_compress_fp8", "fkv_attend_fp8",
@@ -242,6 +245,20 @@ def fkv_compress(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask
                             role.ctypes.data, mask.ctypes.data if mask.size else None,
                             int(budget_m), ctypes.byref(out), _ptr(ckv.workspace),
                             ckv.workspace_bytes, _stream(stream)))
+
+
+def fkv_compress_attend(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask,
+                        budget_m: int, ckv: CompressedKV, out, stream=None) -> None:
+    """fkv_compress then fkv_attend (no attention workspace) in one call: the
+    heads without scored frames attend as soon as their frames are copied."""
+    lib = load()
+    role = _host_u8(head_role)
+    mask = _host_u8(static_keep_mask)
+    cs = ckv.struct()
+    _check(lib.fkv_compress_attend(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   role.ctypes.data, mask.ctypes.data if mask.size else None,
+                                   int(budget_m), ctypes.byref(cs), _ptr(ckv.workspace),
+                                   ckv.workspace_bytes, _ptr(out), _stream(stream)))
 
 
 SCRATCH_BYTES = 4 << 20   # FKV_SCRATCH_BYTES

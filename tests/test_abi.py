@@ -172,6 +172,27 @@ def test_compress_argument_errors_before_any_hip_call(lib):
     assert "cap_tokens" in _capture_error(d, kept - 1, ws)
 
 
+def test_compress_attend_argument_errors_before_any_hip_call(lib):
+    """The combined compression and attention call checks the attention
+    output and the compression arguments on the host, like fkv_compress."""
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    role, mask = np.ones(2, np.uint8), np.zeros((2, 4), np.uint8)
+    st, kept, ws = _plan(d, role, mask, 2)
+    assert st == 0
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(cap, ws_bytes, out=fake):
+        ckv = fkv.FkvCkv(fake, fake, fake, fake, fake, None, cap)
+        return lib.fkv_compress_attend(ctypes.byref(d), fake, fake, fake, role.ctypes.data,
+                                       mask.ctypes.data, 2, ctypes.byref(ckv), fake, ws_bytes,
+                                       out, None)
+
+    assert call(kept, ws, out=None) == fkv.FKV_ERR_NULL
+    assert "attend_out" in fkv.fkv_last_error()
+    assert call(kept - 1, ws) == fkv.FKV_ERR_CAPACITY
+    assert call(kept, ws - 1) == fkv.FKV_ERR_WORKSPACE
+
+
 def test_compress_noalloc_argument_errors_before_any_hip_call(lib):
     """The allocation-free entry point checks its arguments and its scratch
     limit on the host: a layer whose workspace exceeds the library's scratch
