@@ -1,8 +1,12 @@
 """Benchmark of the Forcing-KV hot path on one MI355X.
 
-One step = one pass of the whole path over one attention layer: fkv_compress
-(score dynamic heads, select frames, compact K/V) then fkv_attend (the
-current chunk's queries over the compressed cache).  Inputs are seeded
+One step = one pass of the whole path over one attention layer:
+fkv_compress_attend, i.e. fkv_compress (score dynamic heads, select frames,
+compact K/V) then fkv_attend (the current chunk's queries over the
+compressed cache) in one call, which starts the attention of the heads
+without scored frames beside the scoring of the others when the attention
+runs one workgroup per (head, query tile).  The same pass as the two calls
+is reported as breakdown_ms.step_two_calls.  Inputs are seeded
 synthetic tensors already resident in HBM.  The default workload is the
 480P single layer (12 heads, D=128, 1560 tokens per latent frame, 18 history
 + 3 current frames, m=13, every 16th query scored); the 1080P layer is
@@ -47,6 +51,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--clock-warmup", type=float, default=0.5,
+                    help="seconds of untimed steps before the first timed loop of a "
+                         "workload (the GPU's clocks ramp up under load; without it the "
+                         "first loop of a fresh process runs a few percent slow)")
     ap.add_argument("--workload", default="480p_layer")
     ap.add_argument("--secondary", default="1080p_layer",
                     help="second workload to report ('' to skip)")
@@ -63,7 +71,7 @@ def parse():
                          "(comma-separated workload names, '' to skip)")
     ap.add_argument("--profile-only", action="store_true",
                     help="run the timed loop only (for rocprofv3), print nothing else")
-    ap.add_argument("--only", choices=["step", "compress", "attend", "dense", "copy"],
+    ap.add_argument("--only", choices=["step", "two_calls", "compress", "attend", "dense", "copy"],
                     default="step",
                     help="with --profile-only: which call the loop runs ('copy': a plain "
                          "1 GiB device-to-device tensor copy, the reference for counter "
@@ -88,6 +96,20 @@ class Layer:
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         self.out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=dt, device="cuda")
         self.dout = torch.empty_like(self.out)
+
+
+def clock_warmup(fn, layers, seconds, torch):
+    """Untimed calls of fn for about `seconds` (synchronising every 16
+    calls), so that the timed loops that follow run at the clocks of a
+    loaded GPU."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(layers[i % len(layers)])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def time_loop(fn, layers, steps, warmup, torch):
@@ -116,12 +138,18 @@ def measure(wname, args, fkv, torch, W):
         layers = [base] + [Layer(w, inp, fkv, torch, src=base)
                            for _ in range(max(args.copies, 1) - 1)]
 
+    # One step = one layer's compression and attention, as one call
+    # (fkv_compress_attend, the attention workspace of the layer's cache);
+    # the same pass as the two calls fkv_compress + fkv_attend is timed too.
     def step(L):
+        fkv.fkv_compress_attend(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv, L.out)
+
+    def step_two_calls(L):
         fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
         fkv.fkv_attend(L.desc, L.q, L.ckv, L.out)
 
     if args.profile_only:
-        fn = {"step": step,
+        fn = {"step": step, "two_calls": step_two_calls,
               "compress": lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
                                                      w.budget_m, L.ckv),
               "attend": lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv, L.out),
@@ -132,13 +160,9 @@ def measure(wname, args, fkv, torch, W):
                 step(L)
         time_loop(fn, layers, args.steps, args.warmup, torch)
         return None
+    clock_warmup(step, layers, args.clock_warmup, torch)
     ms_step = time_loop(step, layers, args.steps, args.warmup, torch)
-    # the same layer pass as one call (fkv_compress_attend: attention without
-    # a workspace, the unscored heads attending beside the scoring)
-    ms_step_one_call = time_loop(
-        lambda L: fkv.fkv_compress_attend(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m,
-                                          L.ckv, L.out),
-        layers, args.steps, args.warmup, torch)
+    ms_step_two_calls = time_loop(step_two_calls, layers, args.steps, args.warmup, torch)
     ms_compress = time_loop(lambda L: fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask,
                                                        w.budget_m, L.ckv),
                             layers, args.steps, args.warmup, torch)
@@ -159,7 +183,7 @@ def measure(wname, args, fkv, torch, W):
     attn_flop = 4.0 * w.n_q * D * kept
     dense_flop = 4.0 * w.n_q * D * w.n_win * w.num_heads
     elt = 2 if w.dtype == "bf16" else 4
-    return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_step_one_call=ms_step_one_call,
+    return dict(w=w, inp=inp, kept=kept, ms_step=ms_step, ms_step_two_calls=ms_step_two_calls,
                 ms_compress=ms_compress,
                 stage_ms=stage_ms,
                 ms_attend=ms_attend, ms_dense=ms_dense, attn_flop=attn_flop,
@@ -171,7 +195,7 @@ def measure(wname, args, fkv, torch, W):
 
 def measure_multilayer(wname, args, fkv, torch, W, reps):
     """A whole multi-layer pass with every layer resident in HBM: one chunk
-    step of all layers (fkv_compress + fkv_attend per layer, in layer order),
+    step of all layers (fkv_compress_attend per layer, in layer order),
     the same pass's attention alone, and the full-KV attention pass
     (fkv_attend_dense per layer).  Layers are generated on the host by a few
     threads (NumPy releases the interpreter lock in its array loops) and
@@ -194,8 +218,7 @@ def measure_multilayer(wname, args, fkv, torch, W, reps):
             fn(L)
 
     def step(L):
-        fkv.fkv_compress(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv)
-        fkv.fkv_attend(L.desc, L.q, L.ckv, L.out)
+        fkv.fkv_compress_attend(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv, L.out)
 
     ms_pass = time_loop(lambda _: run_pass(step), [None], reps, 1, torch)
     ms_attend = time_loop(lambda _: run_pass(lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv,
@@ -513,7 +536,7 @@ def main():
         "unit": "query tok/s per layer",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "clock_warmup_s": args.clock_warmup,
         "ms_per_step": r["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -532,7 +555,7 @@ def main():
                      "frac": attn_tflops / peak, "traffic": traffic_record("attend", w.name)},
         "breakdown_ms": {"compress": r["ms_compress"], "attend": r["ms_attend"],
                          "attend_dense": r["ms_dense"],
-                         "step_one_call": r["ms_step_one_call"]},
+                         "step_two_calls": r["ms_step_two_calls"]},
         "speedup_vs_full_kv": r["ms_dense"] / r["ms_step"],
         "attention_speedup_vs_full_kv": r["ms_dense"] / r["ms_attend"],
         "kept_fraction_of_history_kv": r["kept_frac_hist"],
@@ -547,7 +570,7 @@ def main():
             "unit": "query tok/s per layer", "ms_per_step": r2["ms_step"],
             "breakdown_ms": {"compress": r2["ms_compress"], "attend": r2["ms_attend"],
                              "attend_dense": r2["ms_dense"],
-                             "step_one_call": r2["ms_step_one_call"]},
+                             "step_two_calls": r2["ms_step_two_calls"]},
             "attend_tflops": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12,
             "attend_frac_of_peak": r2["attn_flop"] / (r2["ms_attend"] * 1e-3) / 1e12 / peak,
             "speedup_vs_full_kv": r2["ms_dense"] / r2["ms_step"],

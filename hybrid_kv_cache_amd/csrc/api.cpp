@@ -631,21 +631,44 @@ fkv_status_t fkv_compress_attend(const fkv_desc_t *desc, const void *q, const vo
                                  const void *v_cache, const uint8_t *head_role,
                                  const uint8_t *static_keep_mask, int32_t budget_m,
                                  const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
-                                 void *attend_out, void *stream) {
+                                 void *attend_out, void *attend_workspace,
+                                 size_t attend_workspace_bytes, void *stream) {
   Plan p;
   fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
   if (st != FKV_OK) return st;
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   if (!attend_out) return fail(FKV_ERR_NULL, "attend_out is NULL");
+  st = check_compress_out(p, q, out);
+  if (st != FKV_OK) return st;
+  if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
+    return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  if (attend_workspace && desc->dtype == FKV_BF16) {
+    const size_t need = fkv::attend_part_bytes();
+    if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
+    if (attend_workspace_bytes < need)
+      return fail(FKV_ERR_WORKSPACE, "attention workspace of %zu bytes, %zu needed",
+                  attend_workspace_bytes, need);
+  }
   const fkv::WinView win = plain_window(desc, k_cache, v_cache);
-  if (desc->dtype == FKV_BF16)
-    return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
-                           nullptr, true, attend_out);
-  // fp32: the compression, then the attention of every head
+  if (desc->dtype == FKV_BF16) {
+    // With one workgroup per (head, query tile) the attention of the heads
+    // without scored frames can start beside the scoring; the balanced
+    // schedules run over all heads at once, after the compression.
+    fkv::AttendArgs a;
+    a.n_q = p.n_q;
+    a.H = p.H;
+    a.D = p.D;
+    a.n_sel = 0;
+    if (fkv::attend_bf16_schedule(a, attend_workspace, attend_workspace_bytes) == 0)
+      return compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
+                             nullptr, true, attend_out);
+  }
   st = compress_common(desc, p, q, win, out, workspace, workspace_bytes, stream, nullptr,
                        nullptr, true);
   if (st != FKV_OK) return st;
-  return attend_common(desc, q, out->k, out->v, out->tok_off, attend_out, nullptr, 0, stream);
+  return attend_common(desc, q, out->k, out->v, out->tok_off, attend_out, attend_workspace,
+                       attend_workspace_bytes, stream);
 }
 
 fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const void *k_cache,

@@ -608,32 +608,35 @@ size_t attend_part_bytes() {
   return (size_t)2 * 2 * device_cus() * kPartFloats * sizeof(float);
 }
 
-hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_bytes,
-                              hipStream_t s) {
-  if (a0.D != kD) return hipErrorInvalidValue;
-  AttendArgs a = a0;
+// Schedule of a bf16 attention launch over all heads (the sched field): 1
+// (split) with a partial-result buffer and at most one pair per CU; 2
+// (rounds) with one and more pairs than resident workgroups when some pairs
+// are left for a last round; else 0, one workgroup per pair.  Fills the
+// schedule fields of a and returns the combine kernel's workgroups (0: none).
+namespace {
+int plan_attend_bf16(AttendArgs &a, void *part, size_t part_bytes) {
   const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
   // Two workgroups fit on a CU (64 KiB of LDS each).  The split schedule
   // runs exactly that many, all resident at once, when there is at most one
-  // pair per CU; otherwise whole pairs are dealt out as workgroups finish.
-  // With more pairs than resident workgroups, whole pairs are dealt out in
-  // rounds and the remainder halved so that the last round is full too
-  // (xcd_rounds); the halves need 2 slots each, at most nb / 2 of them.
+  // pair per CU.  With more pairs than resident workgroups, whole pairs are
+  // dealt out in rounds and the remainder halved so that the last round is
+  // full too (xcd_rounds); the halves need 2 slots each, at most nb / 2 of
+  // them.
   const int nb = 2 * device_cus();
   a.part = nullptr;
   a.n_wg = pairs;
   a.sched = 0;
   a.slots_x = 0;
   a.cut_max = 0;
-  int combine_blocks = 0;
   const bool have_part = part && nb > 0 && nb % 8 == 0 &&
                          part_bytes >= (size_t)2 * nb * kPartFloats * sizeof(float);
   if (have_part && 2 * pairs <= nb) {
     a.part = static_cast<float *>(part);
     a.n_wg = nb;
     a.sched = 1;
-    combine_blocks = pairs;
-  } else if (have_part && pairs > nb) {
+    return pairs;
+  }
+  if (have_part && pairs > nb) {
     int cut_max = 0, per_x = 0;
     for (int x = 0; x < 8; ++x) {
       const XcdRounds xr = xcd_rounds(pairs, nb / 8, x);
@@ -646,9 +649,24 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
       a.sched = 2;
       a.slots_x = nb / 8;
       a.cut_max = cut_max;
-      combine_blocks = 8 * cut_max;
+      return 8 * cut_max;
     }
   }
+  return 0;
+}
+}  // namespace
+
+int attend_bf16_schedule(const AttendArgs &a0, void *part, size_t part_bytes) {
+  AttendArgs a = a0;
+  plan_attend_bf16(a, part, part_bytes);
+  return a.sched;
+}
+
+hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_bytes,
+                              hipStream_t s) {
+  if (a0.D != kD) return hipErrorInvalidValue;
+  AttendArgs a = a0;
+  const int combine_blocks = plan_attend_bf16(a, part, part_bytes);
   hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
   if (combine_blocks > 0)
     hipLaunchKernelGGL(attend_combine_kernel, dim3(combine_blocks), dim3(256), 0, s, a);

@@ -164,6 +164,9 @@ hipError_t launch_compact_fixed(const FixedCopyPlan &p, hipStream_t s);
 size_t attend_part_bytes();
 // part / part_bytes: null / 0 for one workgroup per (head, query tile).
 hipError_t launch_attend_bf16(const AttendArgs &a, void *part, size_t part_bytes, hipStream_t s);
+// The schedule launch_attend_bf16 would pick (AttendArgs.sched) for a and the
+// partial-result buffer.
+int attend_bf16_schedule(const AttendArgs &a, void *part, size_t part_bytes);
 // The heads a.sel[0 .. a.n_sel) of the ragged cache, one workgroup per pair.
 hipError_t launch_attend_bf16_heads(const AttendArgs &a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s);

@@ -80,7 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fkv_compress.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                  ctypes.POINTER(FkvCkv), P, SZ, P]
     lib.fkv_compress_attend.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
-                                        ctypes.POINTER(FkvCkv), P, SZ, P, P]
+                                        ctypes.POINTER(FkvCkv), P, SZ, P, P, SZ, P]
     lib.fkv_compress_noalloc.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
                                          ctypes.POINTER(FkvCkv), P]
     lib.fkv_compress_timed.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32,
@@ -248,17 +248,20 @@ def fkv_compress(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask
 
 
 def fkv_compress_attend(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_mask,
-                        budget_m: int, ckv: CompressedKV, out, stream=None) -> None:
-    """fkv_compress then fkv_attend (no attention workspace) in one call: the
-    heads without scored frames attend as soon as their frames are copied."""
+                        budget_m: int, ckv: CompressedKV, out, workspace="ckv",
+                        stream=None) -> None:
+    """fkv_compress then fkv_attend in one call (workspace: the attention
+    workspace as for fkv_attend; "ckv" = the one allocated with ckv)."""
     lib = load()
     role = _host_u8(head_role)
     mask = _host_u8(static_keep_mask)
     cs = ckv.struct()
+    ws, ws_bytes = _ws(ckv.attend_ws if isinstance(workspace, str) else workspace)
     _check(lib.fkv_compress_attend(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                    role.ctypes.data, mask.ctypes.data if mask.size else None,
                                    int(budget_m), ctypes.byref(cs), _ptr(ckv.workspace),
-                                   ckv.workspace_bytes, _ptr(out), _stream(stream)))
+                                   ckv.workspace_bytes, _ptr(out), ws, ws_bytes,
+                                   _stream(stream)))
 
 
 SCRATCH_BYTES = 4 << 20   # FKV_SCRATCH_BYTES

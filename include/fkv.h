@@ -129,23 +129,26 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
                           const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
                           void *stream);
 
-/* fkv_compress followed by fkv_attend (without an attention workspace) in
- * one call ([S] 方法 › 输入与整体流程: per layer, the cache is compressed and
- * the current chunk attends over it): the same compressed cache in *out and
- * the same attention output in attend_out [Nq, H, D] (element type of q),
- * bit for bit.  A head's attention depends only on its own compressed rows,
- * so with bf16 the heads that have no scored frames (static heads, and
- * dynamic heads without history) start their attention on the library's
- * side stream as soon as their frames are copied, beside the scoring and
- * selection of the other heads, whose attention follows their copies on the
- * given stream; the call is ordered on the given stream as a whole.
- * Arguments and errors as for fkv_compress; attend_out NULL is
- * FKV_ERR_NULL. */
+/* fkv_compress followed by fkv_attend in one call ([S] 方法 › 输入与整体流程:
+ * per layer, the cache is compressed and the current chunk attends over it):
+ * the same compressed cache in *out and the same attention output in
+ * attend_out [Nq, H, D] (element type of q), bit for bit, as those two calls
+ * with the same attention workspace (attend_workspace / _bytes: optional, as
+ * for fkv_attend).  A head's attention depends only on its own compressed
+ * rows, so with bf16, when the attention runs one workgroup per (head,
+ * 128-query tile), the heads without scored frames (static heads, dynamic
+ * heads without history) start their attention on the library's side stream
+ * as soon as their frames are copied, beside the scoring and selection of
+ * the other heads, whose attention follows their copies on the given stream;
+ * with a balanced attention schedule the two stages run one after the other.
+ * The call is ordered on the given stream as a whole.  Arguments and errors
+ * as for fkv_compress and fkv_attend; attend_out NULL is FKV_ERR_NULL. */
 fkv_status_t fkv_compress_attend(const fkv_desc_t *desc, const void *q, const void *k_cache,
                                  const void *v_cache, const uint8_t *head_role,
                                  const uint8_t *static_keep_mask, int32_t budget_m,
                                  const fkv_ckv_t *out, void *workspace, size_t workspace_bytes,
-                                 void *attend_out, void *stream);
+                                 void *attend_out, void *attend_workspace,
+                                 size_t attend_workspace_bytes, void *stream);
 
 /* fkv_compress without a workspace argument, for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,

@@ -185,7 +185,7 @@ def test_compress_attend_argument_errors_before_any_hip_call(lib):
         ckv = fkv.FkvCkv(fake, fake, fake, fake, fake, None, cap)
         return lib.fkv_compress_attend(ctypes.byref(d), fake, fake, fake, role.ctypes.data,
                                        mask.ctypes.data, 2, ctypes.byref(ckv), fake, ws_bytes,
-                                       out, None)
+                                       out, None, 0, None)
 
     assert call(kept, ws, out=None) == fkv.FKV_ERR_NULL
     assert "attend_out" in fkv.fkv_last_error()

@@ -1,8 +1,10 @@
 """GPU: fkv_compress_attend (compression and attention of one layer in one
-call, the heads without scored frames attending on the library's side stream
-beside the scoring of the others) against fkv_compress followed by fkv_attend
-without a workspace, bitwise: the compressed cache, its offsets and the
-attention output.  One small case is also checked against the oracle."""
+call; with one workgroup per (head, query tile) the heads without scored
+frames attend on the library's side stream beside the scoring of the others)
+against fkv_compress followed by fkv_attend with the same attention
+workspace (none, or the balanced schedules'), bitwise: the compressed cache,
+its offsets and the attention output.  One small case is also checked
+against the oracle."""
 import numpy as np
 import pytest
 
@@ -29,7 +31,9 @@ def _written(w, ckv):
                 .view(np.uint32))
 
 
-def _both(w, inp, role=None, mask=None):
+def _both(w, inp, role=None, mask=None, ws=None):
+    """ws: None (no attention workspace) or "ckv" (the one CompressedKV
+    allocates, which selects a balanced schedule where one applies)."""
     import torch
     role = inp.head_role if role is None else role
     mask = inp.static_keep_mask if mask is None else mask
@@ -40,11 +44,11 @@ def _both(w, inp, role=None, mask=None):
     out_ref = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=dt, device="cuda")
     G.announce(f"fkv_compress + fkv_attend {w.name} roles={list(role)}")
     fkv.fkv_compress(desc, q, k, v, role, mask, w.budget_m, ref)
-    fkv.fkv_attend(desc, q, ref, out_ref, None)
+    fkv.fkv_attend(desc, q, ref, out_ref, ws)
     got = fkv.CompressedKV(desc, role, mask, w.budget_m)
     out = torch.empty_like(out_ref)
     G.announce(f"fkv_compress_attend {w.name}")
-    fkv.fkv_compress_attend(desc, q, k, v, role, mask, w.budget_m, got, out)
+    fkv.fkv_compress_attend(desc, q, k, v, role, mask, w.budget_m, got, out, ws)
     torch.cuda.synchronize()
     a, b = _written(w, ref), _written(w, got)
     for key in a:
@@ -54,13 +58,22 @@ def _both(w, inp, role=None, mask=None):
     return got, out
 
 
-def test_480p_layer_matches_two_calls():
+@pytest.mark.parametrize("ws", [None, "ckv"])
+def test_480p_layer_matches_two_calls(ws):
     w = W.WORKLOADS["480p_layer"]
-    _both(w, W.generate_layer(w, 0))
+    _both(w, W.generate_layer(w, 0), ws=ws)
 
 
+def test_1080p_layer_matches_two_calls_with_rounds_schedule():
+    """More (head, query tile) pairs than resident workgroups: with the
+    workspace the attention runs the rounds schedule after the compression."""
+    w = W.WORKLOADS["1080p_layer"]
+    _both(w, W.generate_layer(w, 0), ws="ckv")
+
+
+@pytest.mark.parametrize("ws", [None, "ckv"])
 @pytest.mark.parametrize("case", ["mixed", "all_static", "all_dynamic", "no_history"])
-def test_small_role_mixes_match_two_calls(case):
+def test_small_role_mixes_match_two_calls(case, ws):
     Fh = 0 if case == "no_history" else 7
     w = W.small_workload(tokens_per_frame=150, num_heads=6, hist_frames=Fh, budget_m=min(3, Fh),
                          num_static=2, query_stride=5, seed=71)
@@ -70,7 +83,7 @@ def test_small_role_mixes_match_two_calls(case):
         role[:] = fkv.FKV_STATIC
     elif case in ("all_dynamic", "no_history"):
         role[:] = fkv.FKV_DYNAMIC
-    _both(w, inp, role=role)
+    _both(w, inp, role=role, ws=ws)
 
 
 def test_fp32_matches_two_calls_and_oracle():
