@@ -220,6 +220,7 @@ def measure_multilayer(wname, args, fkv, torch, W, reps):
     def step(L):
         fkv.fkv_compress_attend(L.desc, L.q, L.k, L.v, L.role, L.mask, w.budget_m, L.ckv, L.out)
 
+    clock_warmup(lambda _: run_pass(step), [None], args.clock_warmup, torch)
     ms_pass = time_loop(lambda _: run_pass(step), [None], reps, 1, torch)
     ms_attend = time_loop(lambda _: run_pass(lambda L: fkv.fkv_attend(L.desc, L.q, L.ckv,
                                                                       L.out)),
