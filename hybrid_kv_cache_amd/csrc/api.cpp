@@ -368,8 +368,9 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   SideStream *ss = nullptr;
   std::unique_lock<std::mutex> side_lock;
   // Joins the side stream into the caller's stream on every return after
-  // the fork (before the lock is released); the dynamic compaction joins
-  // explicitly.
+  // the fork (before the lock is released).  Without attend_out the join is
+  // made explicitly before the dynamic heads' copies; with it, on return
+  // (the scored heads' attention waits only for the fixed copies).
   struct Join {
     hipStream_t s = nullptr;
     hipEvent_t ev = nullptr;
