@@ -342,7 +342,7 @@ hipError_t attend_heads(const fkv_desc_t *d, const Plan &p, const void *q, const
 // (plain or rolling) with the plan p.
 // kv_scales (host [2 H]: K scales, then V scales) selects an e4m3 cache.
 // side: copy the compaction jobs that do not depend on the scores on the
-// device's side stream, beside the scoring (not with kv_scales or ev).
+// device's side stream, beside the scoring (not with ev).
 // attend_out (bf16, with side): also the attention of the compressed cache
 // into attend_out [Nq, H, D], one workgroup per (head, 128-query tile): the
 // heads whose copies are all fixed by the plan right after those copies on
@@ -364,7 +364,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   fkv::CopySlot *slots = reinterpret_cast<fkv::CopySlot *>(ws + p.ws_slot_off);
   const float c = log2e_scale(*desc);
 
-  const bool split = side && !kv_scales && !ev;
+  const bool split = side && !ev;
   SideStream *ss = nullptr;
   std::unique_lock<std::mutex> side_lock;
   // Joins the side stream into the caller's stream on every return after
@@ -428,7 +428,18 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     std::memcpy(cp.kept, p.kept, sizeof(cp.kept));
     std::memcpy(cp.static_bits, p.static_bits, sizeof(cp.static_bits));
     std::memcpy(cp.tok_off_h, p.tok_off, sizeof(cp.tok_off_h));
-    hipError_t el = fkv::launch_compact_fixed(cp, ss->s);
+    hipError_t el;
+    if (kv_scales) {
+      fkv::Fp8Scales sc;
+      sc.D = p.D;
+      for (int h = 0; h < fkv::kMaxHeads; ++h) {
+        sc.k_scale[h] = h < p.H ? kv_scales[h] : 1.f;
+        sc.v_scale[h] = h < p.H ? kv_scales[p.H + h] : 1.f;
+      }
+      el = fkv::launch_compact_fp8_fixed(cp, sc, ss->s);
+    } else {
+      el = fkv::launch_compact_fixed(cp, ss->s);
+    }
     if (attend_out && el == hipSuccess) {
       // The heads with no scored frames are complete once the fixed copies
       // are: their attention starts here, beside the scoring and selection.
@@ -491,7 +502,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
       ca.k_scale[h] = h < p.H ? kv_scales[h] : 1.f;
       ca.v_scale[h] = h < p.H ? kv_scales[p.H + h] : 1.f;
     }
-    hipError_t e = fkv::launch_compact_fp8(ca, p.slot_off[p.H], s);
+    hipError_t e = fkv::launch_compact_fp8(ca, split ? p.dyn_slot_off[p.H] : p.slot_off[p.H], s);
     if (e != hipSuccess) return hip_fail(e, "quantizing compaction kernel launch");
   } else {
     fkv::CompactArgs ca;
@@ -720,7 +731,7 @@ fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void 
   if (st != FKV_OK) return st;
   if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
-                         workspace_bytes, stream, kv_scales);
+                         workspace_bytes, stream, kv_scales, nullptr, true);
 }
 
 fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,

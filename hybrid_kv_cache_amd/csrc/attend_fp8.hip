@@ -311,24 +311,25 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
   }
 }
 
-// Quantizing compaction: workgroup b copies rows [64 c, 64 c + 64) of slot
-// b / chunks; a thread turns 8 bf16 values (16 bytes) into 8 e4m3 bytes.
-__global__ __launch_bounds__(256) void compact_fp8_kernel(CompactFp8Args a) {
-  const int slot = blockIdx.x / a.chunks;
-  const int cidx = blockIdx.x - slot * a.chunks;
-  const CopySlot sl = a.slots[slot];
+// Quantizing copy of rows [64 c, 64 c + 64) (clipped to T) of one
+// compaction job: the K and V rows of window frame sl.src_frame of head
+// sl.head go, as e4m3 codes of x / scale, to compacted rows sl.dst_row +
+// 64 c ... of k_out / v_out; a thread turns 8 bf16 values (16 bytes) into 8
+// e4m3 bytes.
+__device__ __forceinline__ void quantize_rows(const WinView &win, int fh_h, CopySlot sl, int cidx,
+                                              int T, int D, float sk, float sv, uint8_t *k_out,
+                                              uint8_t *v_out) {
   const int r0 = cidx * kCompactRows;
-  const int nrows = min(kCompactRows, a.T - r0);
-  const int pieces = a.D / 8;                 // 16-byte bf16 pieces per row
+  const int nrows = min(kCompactRows, T - r0);
+  const int pieces = D / 8;                 // 16-byte bf16 pieces per row
   const int items = nrows * pieces;
   int64_t stride;
-  const char *ks = frame_rows(a.win, false, sl.head, a.fh[sl.head], sl.src_frame, a.T, &stride);
-  const char *vs = frame_rows(a.win, true, sl.head, a.fh[sl.head], sl.src_frame, a.T, &stride);
-  const float sk = a.k_scale[sl.head], sv = a.v_scale[sl.head];
+  const char *ks = frame_rows(win, false, sl.head, fh_h, sl.src_frame, T, &stride);
+  const char *vs = frame_rows(win, true, sl.head, fh_h, sl.src_frame, T, &stride);
   for (int i = threadIdx.x; i < items; i += 256) {
     const int r = i / pieces, p = i - r * pieces;
     const int64_t so = (int64_t)(r0 + r) * stride + p * 16;
-    const int64_t d = (sl.dst_row + r0 + r) * (int64_t)a.D + p * 8;
+    const int64_t d = (sl.dst_row + r0 + r) * (int64_t)D + p * 8;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const u32x4 x = ld16((kv ? vs : ks) + so);
@@ -344,9 +345,31 @@ __global__ __launch_bounds__(256) void compact_fp8_kernel(CompactFp8Args a) {
         int v = cvt2<false>(f0, f1, 0);
         w[e] = (uint32_t)cvt2<true>(f2, f3, v);
       }
-      *reinterpret_cast<u32x2 *>((kv ? a.v_out : a.k_out) + d) = w;
+      *reinterpret_cast<u32x2 *>((kv ? v_out : k_out) + d) = w;
     }
   }
+}
+
+// Quantizing compaction of the slots the selection wrote: workgroup b
+// copies chunk b % chunks of slot b / chunks.
+__global__ __launch_bounds__(256) void compact_fp8_kernel(CompactFp8Args a) {
+  const int slot = blockIdx.x / a.chunks;
+  const int cidx = blockIdx.x - slot * a.chunks;
+  const CopySlot sl = a.slots[slot];
+  quantize_rows(a.win, a.fh[sl.head], sl, cidx, a.T, a.D, a.k_scale[sl.head],
+                a.v_scale[sl.head], a.k_out, a.v_out);
+}
+
+// The quantizing copies the plan fixes (static heads' kept frames, every
+// head's current chunk; see fixed_slot): workgroup b copies chunk
+// b % chunks of job b / chunks.
+__global__ __launch_bounds__(256) void compact_fp8_fixed_kernel(FixedCopyPlan p, Fp8Scales sc) {
+  const int job = blockIdx.x / p.chunks;
+  const int cidx = blockIdx.x - job * p.chunks;
+  const CopySlot sl = fixed_slot(p, job);
+  quantize_rows(p.win, p.fh[sl.head], sl, cidx, p.T, sc.D, sc.k_scale[sl.head],
+                sc.v_scale[sl.head], reinterpret_cast<uint8_t *>(p.k_out),
+                reinterpret_cast<uint8_t *>(p.v_out));
 }
 
 }  // namespace
@@ -354,6 +377,14 @@ __global__ __launch_bounds__(256) void compact_fp8_kernel(CompactFp8Args a) {
 hipError_t launch_attend_fp8(const AttendFp8Args &a, hipStream_t s) {
   const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
   hipLaunchKernelGGL(attend_fp8_kernel, dim3(pairs), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_fp8_fixed(const FixedCopyPlan &p, const Fp8Scales &sc, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.fixed_off_h[p.H] * p.chunks;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_fp8_fixed_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, sc);
   return hipGetLastError();
 }
 

@@ -21,6 +21,14 @@ struct CompactFp8Args {
   float v_scale[kMaxHeads];
 };
 
+// Per-head e4m3 scales of K and V and the head dimension, for the
+// quantizing copies of the fixed compaction jobs.
+struct Fp8Scales {
+  int32_t D;
+  float k_scale[kMaxHeads];
+  float v_scale[kMaxHeads];
+};
+
 // fp8 attention over an e4m3 compressed cache (D = 128).  Queries are bf16
 // and quantized per head in the kernel (q / q_scale[h]); scores are
 // (q_hat . k_hat) q_scale k_scale, values v_hat v_scale.
@@ -37,6 +45,8 @@ struct AttendFp8Args {
 };
 
 hipError_t launch_compact_fp8(const CompactFp8Args &a, int total_slots, hipStream_t s);
+// The quantizing copies of the fixed compaction jobs of p.
+hipError_t launch_compact_fp8_fixed(const FixedCopyPlan &p, const Fp8Scales &sc, hipStream_t s);
 hipError_t launch_attend_fp8(const AttendFp8Args &a, hipStream_t s);
 
 }  // namespace fkv

@@ -29,13 +29,15 @@
  * error string (and the scratch array of fkv_compress_noalloc); every device
  * operation is enqueued on the given stream (a hipStream_t passed as void*,
  * NULL = the default stream) and no call waits for the device.  The one
- * exception to a single stream: fkv_compress and fkv_compress_ragged run the
- * copies that do not depend on the scores on a second stream of the library
- * (one per device, non-blocking, default priority, created with two events
- * on the first such call and kept until the process ends), forked from the
- * given stream by an event before the scoring and joined back into it before
- * the remaining copies, so that to the caller the call is still ordered on
- * its stream like a single kernel sequence.  Calls from several host threads
+ * exception to a single stream: fkv_compress, fkv_compress_ragged,
+ * fkv_compress_fp8 and fkv_compress_attend run the copies that do not depend
+ * on the scores (and fkv_compress_attend some of the attention) on a second
+ * stream of the library (one per device, non-blocking, default priority,
+ * created with three events on the first such call and kept until the
+ * process ends), forked from the given stream by an event before the scoring
+ * and joined back into it by event waits before the call returns, so that
+ * to the caller the call is still ordered on its stream like a single kernel
+ * sequence.  Calls from several host threads
  * are serialised on that stream's per-device lock while they enqueue.  The
  * library allocates no device memory.
  *

@@ -115,3 +115,61 @@ def test_compress_from_two_threads_on_two_streams():
     assert not errors, errors
     for (t, r, l), ckv in outs.items():
         _same(refs[l], _host(w, ckv), f"thread {t} rep {r} layer {l}")
+
+
+def test_compress_attend_from_two_threads_on_two_streams():
+    """fkv_compress_attend (attention of the unscored heads on the side
+    stream, three events per call) from two host threads at once: every
+    cache and attention output equals the two-call result."""
+    import torch
+    w = W.WORKLOADS["480p_30layers"]
+    layers = [W.generate_layer(w, l) for l in range(3)]
+    dev = [G.upload(inp) for inp in layers]
+    desc = fkv.desc_for(w)
+    refs, ref_out = [], []
+    for inp, (q, k, v) in zip(layers, dev):
+        ckv = fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m)
+        out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        fkv.fkv_compress(desc, q, k, v, inp.head_role, inp.static_keep_mask, w.budget_m, ckv)
+        fkv.fkv_attend(desc, q, ckv, out, None)
+        torch.cuda.synchronize()
+        refs.append(_host(w, ckv))
+        ref_out.append(fkv.to_host(out).view(np.uint16).copy())
+    reps = 3
+    outs = {}
+    for t in range(2):
+        for r in range(reps):
+            for l, inp in enumerate(layers):
+                outs[(t, r, l)] = (
+                    fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m),
+                    torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=torch.bfloat16,
+                                device="cuda"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+
+    def worker(t):
+        try:
+            for r in range(reps):
+                for l, inp in enumerate(layers):
+                    q, k, v = dev[l]
+                    ckv, out = outs[(t, r, l)]
+                    fkv.fkv_compress_attend(desc, q, k, v, inp.head_role, inp.static_keep_mask,
+                                            w.budget_m, ckv, out, None, stream=streams[t])
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    G.announce(f"fkv_compress_attend {w.name} from 2 threads x {reps} x {len(layers)} layers")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for st in streams:
+        st.synchronize()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (t, r, l), (ckv, out) in outs.items():
+        _same(refs[l], _host(w, ckv), f"thread {t} rep {r} layer {l}")
+        assert np.array_equal(ref_out[l], fkv.to_host(out).view(np.uint16)), \
+            f"attention output, thread {t} rep {r} layer {l}"
