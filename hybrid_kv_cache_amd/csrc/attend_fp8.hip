@@ -321,13 +321,14 @@ __device__ __forceinline__ void quantize_rows(const WinView &win, int fh_h, Copy
                                               uint8_t *v_out) {
   const int r0 = cidx * kCompactRows;
   const int nrows = min(kCompactRows, T - r0);
-  const int pieces = D / 8;                 // 16-byte bf16 pieces per row
+  const int pieces = D / 8;                 // 16-byte bf16 pieces per row (16)
+  const int pieces_shift = __builtin_ctz((unsigned)pieces);
   const int items = nrows * pieces;
   int64_t stride;
   const char *ks = frame_rows(win, false, sl.head, fh_h, sl.src_frame, T, &stride);
   const char *vs = frame_rows(win, true, sl.head, fh_h, sl.src_frame, T, &stride);
   for (int i = threadIdx.x; i < items; i += 256) {
-    const int r = i / pieces, p = i - r * pieces;
+    const int r = i >> pieces_shift, p = i & (pieces - 1);
     const int64_t so = (int64_t)(r0 + r) * stride + p * 16;
     const int64_t d = (sl.dst_row + r0 + r) * (int64_t)D + p * 8;
 #pragma unroll

@@ -229,6 +229,9 @@ __device__ __forceinline__ void copy_rows(const WinView &win, int fh_h, CopySlot
   const int nrows = min(kCompactRows, T - r0);
   const int row_bytes = win.row_bytes;
   const int v16 = row_bytes >> 4;          // 16-byte pieces per row
+  // rows are 128, 256 or 512 bytes (D of 64 or 128, bf16 or fp32): a power
+  // of two, so row and piece come from a shift and a mask
+  const int v16_shift = __builtin_ctz((unsigned)v16);
   const int items = nrows * v16;
   int64_t src_stride;
   const char *ks = frame_rows(win, false, sl.head, fh_h, sl.src_frame, T, &src_stride) +
@@ -244,7 +247,7 @@ __device__ __forceinline__ void copy_rows(const WinView &win, int fh_h, CopySlot
     for (int u = 0; u < U; ++u) {
       const int idx = base + u * kThreads + threadIdx.x;
       if (idx < items) {
-        const int r = idx / v16, p = idx - r * v16;
+        const int r = idx >> v16_shift, p = idx & (v16 - 1);
         const int64_t so = r * src_stride + p * 16;
         kr[u] = ld16_stream(ks + so);
         vr[u] = ld16_stream(vs + so);

@@ -307,12 +307,13 @@ __global__ __launch_bounds__(256) void gather_kernel(TokenArgs a) {
   if (r0 >= n) return;
   const int rows = (int)min((int64_t)64, n - r0);
   const int row_bytes = a.D * a.elt;
-  const int v16 = row_bytes >> 4;
+  const int v16 = row_bytes >> 4;                 // a power of two (D 64 or 128)
+  const int v16_shift = __builtin_ctz((unsigned)v16);
   const int64_t tm = (int64_t)a.H * row_bytes;
   const char *kb = reinterpret_cast<const char *>(a.k) + (int64_t)h * row_bytes;
   const char *vb = reinterpret_cast<const char *>(a.v) + (int64_t)h * row_bytes;
   for (int i = threadIdx.x; i < rows * v16; i += 256) {
-    const int r = i / v16, p = i - r * v16;
+    const int r = i >> v16_shift, p = i & (v16 - 1);
     const int64_t t = a.src[lo + r0 + r];
     const int64_t so = t * tm + p * 16;
     const int64_t d = (lo + r0 + r) * row_bytes + p * 16;
