@@ -131,6 +131,10 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
     f32x16 s[2];
     s[0] = f32x16{};
     s[1] = f32x16{};
+    // Issue priority 1 while this wave reads its K fragments and feeds the
+    // MFMAs, back to 0 for the softmax: the two waves sharing a SIMD take
+    // turns, one's exponentials beside the other's MFMAs.
+    __builtin_amdgcn_s_setprio(1);
     u32x4 kf[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) kf[i] = lds_read_b128(kl, kbase[i >> 1] + (i & 1) * 32 * 256);
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_s_setprio(0);
 
     if (valid < kKT) {
 #pragma unroll
