@@ -12,8 +12,10 @@
 // (with all logits 0, every frame's value is exactly log2(T)).
 //
 // bf16 kernel: workgroup = 4 waves x 32 sampled queries, one frame of one
-// dynamic head; K rows of the frame are copied straight into a four-slot LDS
-// ring in tiles of 64 (three tiles in flight ahead of the one being read);
+// dynamic head; K rows of the frame are copied straight into a two-slot LDS
+// ring in tiles of 64 (the next tile in flight while one is read; 32 KB of
+// LDS, so four workgroups share a CU and hide the copies' latency -- deeper
+// rings at two workgroups per CU measured 5-10% slower);
 // S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  Frames are located through the
 // window view: a plain token-major window, or a head's ragged history (a
 // previous compressed cache) followed by the current chunk.  Head profiling
@@ -29,7 +31,7 @@ constexpr int kKT = 64;
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
 constexpr int kTileBytes = KvTileLds<kKT>::kBytes;
-constexpr int kAhead = 3;              // tiles in flight ahead of the one read (<= 3)
+constexpr int kAhead = 1;              // tiles in flight ahead of the one read (<= 3)
 constexpr int kRing = kAhead + 1;
 
 // Wait until at most `tiles` tile copies (4 loads each) of this wave remain
@@ -43,7 +45,7 @@ __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-__global__ __launch_bounds__(256, 2) void score_bf16_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, 4) void score_bf16_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing * kTileBytes];
   typedef KvTileLds<kKT> Lds;
   const int tid = threadIdx.x;
