@@ -273,13 +273,14 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     if (it + 1 < t1) issue(vrsrc, it + 1, v_fill);
     const int valid = kv.len - it * kKT;
     if (valid < kKT) {  // ragged last tile: keys past the end get no weight
+      // key = kb * 32 + 8 (r >> 2) + (r & 3) + 4 g: the lane's part moves to
+      // the bound, so each test compares a constant with one register.
+      const int bound = valid - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= valid) sc[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= bound) sc[kb][r] = -INFINITY;
     }
     // Exact maximum of this tile's scaled scores (lane pair combined).
     auto tile_max = [&]() {

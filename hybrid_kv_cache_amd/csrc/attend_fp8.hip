@@ -200,11 +200,14 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
     if (it + 1 < ntiles) issue(vrsrc, it + 1, v_fill);
     const int valid = len - it * kKT;
     if (valid < kKT) {
+      // The lane's part of the key index (32 g) moves to the bound, so each
+      // test compares a constant with one register.
+      const int bound = valid - 32 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * g + 16 * kb + r >= valid) sc[kb][r] = -INFINITY;
+          if (16 * kb + r >= bound) sc[kb][r] = -INFINITY;
     }
     // Reference: the first tile's maximum, raised whenever a tile's maximum
     // passes it by more than 8 (weights stay <= 2^8).

@@ -153,13 +153,14 @@ __global__ __launch_bounds__(256, 4) void score_bf16_kernel(ScoreArgs a) {
     __builtin_amdgcn_s_setprio(0);
 
     if (valid < kKT) {
+      // key = kb * 32 + 8 (q >> 2) + (q & 3) + 4 g: the lane's part moves to
+      // the bound, so each test compares a constant with one register.
+      const int bound = valid - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int key = kb * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-          if (key >= valid) s[kb][q] = -INFINITY;
-        }
+        for (int q = 0; q < 16; ++q)
+          if (kb * 32 + 8 * (q >> 2) + (q & 3) >= bound) s[kb][q] = -INFINITY;
     }
     // Per-lane running sum of 2^(c s - m).  The reference m is this lane's
     // first-tile maximum and is raised only when a tile's sum passes 2^64 (or
