@@ -329,18 +329,19 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
     qk(k_read, sn);
     weights();
     // K-fragment reads run four ahead of the 16 score MFMAs of the next
-    // tile, each followed by a slice of this tile's softmax.
+    // tile, each followed by a slice of up to eight of this tile's softmax
+    // instructions (the softmax is spent by the last few MFMAs).
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     if (__any(!(lt <= 0x1p64f))) {
