@@ -252,10 +252,11 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, flags);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ec, flags);
     if (e != hipSuccess) {
-      if (ec) hipEventDestroy(ec);
-      if (ej) hipEventDestroy(ej);
-      if (ef) hipEventDestroy(ef);
-      if (st) hipStreamDestroy(st);
+      // Best-effort cleanup; the creation error is the one reported.
+      if (ec) (void)hipEventDestroy(ec);
+      if (ej) (void)hipEventDestroy(ej);
+      if (ef) (void)hipEventDestroy(ef);
+      if (st) (void)hipStreamDestroy(st);
       return e;
     }
     ss.s = st;
@@ -367,17 +368,25 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   const bool split = side && !ev;
   SideStream *ss = nullptr;
   std::unique_lock<std::mutex> side_lock;
-  // Joins the side stream into the caller's stream on every return after
-  // the fork (before the lock is released).  Without attend_out the join is
-  // made explicitly before the dynamic heads' copies; with it, on return
-  // (the scored heads' attention waits only for the fixed copies).
+  // Joins the side stream into the caller's stream after the fork, before
+  // the lock is released.  Without attend_out the join is made before the
+  // dynamic heads' copies, with it at the end (the scored heads' attention
+  // waits only for the fixed copies); both are checked.  On an early error
+  // return the destructor still makes it, as a best effort, so that the
+  // caller's stream never runs ahead of work already enqueued on the side
+  // stream.
   struct Join {
     hipStream_t s = nullptr;
     hipEvent_t ev = nullptr;
-    ~Join() {
-      if (ev) hipStreamWaitEvent(s, ev, 0);
+    hipError_t now() {
+      const hipError_t e = ev ? hipStreamWaitEvent(s, ev, 0) : hipSuccess;
+      ev = nullptr;
+      return e;
     }
+    ~Join() { (void)now(); }
   } join;
+  // Stage boundaries of fkv_compress_timed.
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if (split) {
     // 0. fork point: the side stream starts from the caller's stream as it
     // stands before the scoring
@@ -386,7 +395,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     e = hipEventRecord(ss->fork, s);
     if (e != hipSuccess) return hip_fail(e, "side stream fork");
   }
-  if (ev) hipEventRecord(ev[0], s);
+  if (hipError_t e = mark(0); e != hipSuccess) return hip_fail(e, "timing event");
   // 1. dynamic-head scoring: per (sampled query, frame) log-sum-exp
   hipError_t score_err = hipSuccess;
   if (p.n_dyn > 0) {
@@ -454,7 +463,7 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     if (el != hipSuccess) return hip_fail(el, "side stream launch");
   }
   if (score_err != hipSuccess) return hip_fail(score_err, "scoring kernel launch");
-  if (ev) hipEventRecord(ev[1], s);
+  if (hipError_t e = mark(1); e != hipSuccess) return hip_fail(e, "timing event");
   // 2. selection, offsets and compaction slots
   {
     fkv::SelectArgs sa;
@@ -481,10 +490,9 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     hipError_t e = fkv::launch_select(sa, s);
     if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
   }
-  if (ev) hipEventRecord(ev[2], s);
-  if (join.ev && !attend_out) {
-    const hipError_t e = hipStreamWaitEvent(s, join.ev, 0);
-    join.ev = nullptr;
+  if (hipError_t e = mark(2); e != hipSuccess) return hip_fail(e, "timing event");
+  if (!attend_out) {
+    const hipError_t e = join.now();
     if (e != hipSuccess) return hip_fail(e, "side stream join");
   }
   // 3. compaction
@@ -518,13 +526,15 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
     hipError_t e = fkv::launch_compact(ca, split ? p.dyn_slot_off[p.H] : p.slot_off[p.H], s);
     if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
   }
-  if (ev) hipEventRecord(ev[3], s);
+  if (hipError_t e = mark(3); e != hipSuccess) return hip_fail(e, "timing event");
   if (attend_out && split) {
     // 4. attention of the scored heads, whose current chunk the side stream
-    // copied (the side stream's own attention is joined on return)
+    // copied, then the join of the side stream's own attention
     hipError_t e = hipStreamWaitEvent(s, ss->copied, 0);
     if (e == hipSuccess) e = attend_heads(desc, p, q, out, attend_out, true, s);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    e = join.now();
+    if (e != hipSuccess) return hip_fail(e, "side stream join");
   }
   return ok();
 }
@@ -777,7 +787,7 @@ fkv_status_t fkv_compress_timed(const fkv_desc_t *desc, const void *q, const voi
   for (int i = 0; i < 4; ++i) {
     const hipError_t e = hipEventCreate(&ev[i]);
     if (e != hipSuccess) {
-      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
       return hip_fail(e, "event creation");
     }
   }
@@ -789,7 +799,7 @@ fkv_status_t fkv_compress_timed(const fkv_desc_t *desc, const void *q, const voi
   // No scoring kernel runs without dynamic heads (the two events around the
   // empty stage would only time their own recording).
   if (st == FKV_OK && e == hipSuccess && p.n_dyn == 0) ms[0] = 0.f;
-  for (int i = 0; i < 4; ++i) hipEventDestroy(ev[i]);
+  for (int i = 0; i < 4; ++i) (void)hipEventDestroy(ev[i]);
   if (st != FKV_OK) return st;
   if (e != hipSuccess) return hip_fail(e, "event timing");
   return ok();
@@ -1093,7 +1103,7 @@ fkv_status_t fkv_mfma_peak(int32_t iters, float *sink, double *tflops) {
   hipEvent_t ev[2] = {};
   if ((e = hipEventCreate(&ev[0])) != hipSuccess) return hip_fail(e, "event creation");
   if ((e = hipEventCreate(&ev[1])) != hipSuccess) {
-    hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[0]);
     return hip_fail(e, "event creation");
   }
   const int blocks = 2 * cus;
@@ -1104,8 +1114,8 @@ fkv_status_t fkv_mfma_peak(int32_t iters, float *sink, double *tflops) {
   if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
   float ms = 0.f;
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
-  hipEventDestroy(ev[0]);
-  hipEventDestroy(ev[1]);
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
   if (e != hipSuccess) return hip_fail(e, "MFMA calibration");
   // 4 waves per workgroup, 8 MFMAs of 32 x 32 x 16 (2 FLOP each) per iteration
   const double flop = (double)blocks * 4 * 8 * iters * 2.0 * 32 * 32 * 16;
