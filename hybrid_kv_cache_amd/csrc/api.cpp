@@ -745,14 +745,23 @@ fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void 
 }
 
 fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
-                            const float *scales, void *out, void *stream) {
+                            const float *scales, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;
+  if (desc->dtype != FKV_BF16) return fail(FKV_ERR_DTYPE, "the fp8 attention takes bf16 queries");
   st = check_scales(desc, scales, 3 * desc->num_heads, "scales");
   if (st != FKV_OK) return st;
   if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");
   if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
     return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  if (workspace) {
+    const size_t need = fkv::attend_part_bytes();
+    if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
+    if (workspace_bytes < need)
+      return fail(FKV_ERR_WORKSPACE, "attention workspace of %zu bytes, %zu needed",
+                  workspace_bytes, need);
+  }
   fkv::AttendFp8Args a;
   a.q = q;
   a.k = reinterpret_cast<const uint8_t *>(ckv->k);
@@ -768,7 +777,8 @@ fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv
     a.k_scale[h] = h < H ? scales[H + h] : 1.f;
     a.v_scale[h] = h < H ? scales[2 * H + h] : 1.f;
   }
-  hipError_t e = fkv::launch_attend_fp8(a, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = fkv::launch_attend_fp8(a, workspace, workspace ? workspace_bytes : 0,
+                                        reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 attention kernel launch");
   return ok();
 }

@@ -67,50 +67,6 @@ __device__ __forceinline__ int head_tiles(const AttendArgs &a, int h) {
   return (int)((len + kKT - 1) / kKT);
 }
 
-// Split schedule on XCD x (nb workgroups, nb % 8 == 0, at most nb / 2
-// pairs): the XCD's pairs are [p_lo, p_lo + np) and its workgroups
-// xs = 0 .. nb/8 - 1.  The first np workgroups run tiles [0, split) of one
-// pair each (main parts), the ne others the tails [split, tiles) of up to
-// k = ceil(np / ne) pairs each (k = 0: no cut).
-struct XcdSplit {
-  int p_lo, np, ne, k;
-};
-__device__ __forceinline__ XcdSplit xcd_split(int pairs, int nb, int x) {
-  XcdSplit s;
-  s.p_lo = pairs * x / 8;
-  s.np = pairs * (x + 1) / 8 - s.p_lo;
-  s.ne = nb / 8 - s.np;
-  s.k = s.ne > 0 ? (s.np + s.ne - 1) / s.ne : 0;
-  return s;
-}
-// Rounds schedule on XCD x (more pairs than resident workgroups): the XCD's
-// pairs are [p_lo, p_lo + np) and slots_x workgroups of it run at a time.
-// The first w pairs run whole, one workgroup each, in full rounds plus part
-// of the last; the s pairs after them are cut in two halves (tiles
-// [0, nt/2) and [nt/2, nt)) so that the last round is full too: with
-// rem = np mod slots_x, s = rem when 2 rem <= slots_x (the last round is
-// halves only), else s = slots_x - rem (rem - s whole pairs and 2 s halves).
-struct XcdRounds {
-  int p_lo, np, w, s;
-};
-__host__ __device__ __forceinline__ XcdRounds xcd_rounds(int pairs, int slots_x, int x) {
-  XcdRounds r;
-  r.p_lo = pairs * x / 8;
-  r.np = pairs * (x + 1) / 8 - r.p_lo;
-  const int rem = r.np % slots_x;
-  r.s = rem == 0 ? 0 : (2 * rem <= slots_x ? rem : slots_x - rem);
-  r.w = r.np - r.s;
-  return r;
-}
-
-// First tail tile of a pair with nt tiles (nt when nothing is cut).  A
-// tail workgroup runs its k tails one after the other, each restarting the
-// copy pipeline, and takes about 9/8 the time per tile of a main workgroup;
-// split = nt * 9k / (8 + 9k) evens out the two.
-__device__ __forceinline__ int split_tile(int nt, int k) {
-  return k > 0 ? (int)((int64_t)nt * (9 * k) / (8 + 9 * k)) : nt;
-}
-
 __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   // LDS: two K tiles and two V tiles, each its own array.  Step t (parity
   // P = t & 1) reads K(t+1) from sk[1-P] and V(t) from sv[P] while K(t+2) is
@@ -141,38 +97,10 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(AttendArgs a) {
   //  - With one and more pairs than resident workgroups: the rounds
   //    schedule of xcd_rounds; its halved pairs leave two partial results
   //    in slots 2 (x cut_max + c) and 2 (x cut_max + c) + 1.
-  const int nb = gridDim.x, x = blockIdx.x & 7, xs = blockIdx.x >> 3;
-  int p0, n_items, k = 0, tail = 0, slot0 = -1;
-  if (!a.part) {
-    p0 = x * (nb >> 3) + min(x, nb & 7) + xs;
-    n_items = 1;
-  } else if (a.sched == 2) {
-    const XcdRounds xr = xcd_rounds(pairs, a.slots_x, x);
-    n_items = 1;
-    if (xs < xr.w) {
-      p0 = xr.p_lo + xs;
-    } else if (xs < xr.w + 2 * xr.s) {
-      const int c = (xs - xr.w) >> 1;
-      tail = (xs - xr.w) & 1;
-      p0 = xr.p_lo + xr.w + c;
-      k = -1;  // halves
-      slot0 = 2 * (x * a.cut_max + c);
-    } else {
-      return;  // padding: XCDs with fewer pairs
-    }
-  } else {
-    const XcdSplit sp = xcd_split(pairs, nb, x);
-    k = sp.k;
-    if (xs < sp.np) {
-      p0 = sp.p_lo + xs;
-      n_items = 1;
-    } else {
-      const int e = xs - sp.np;
-      p0 = sp.p_lo + e * sp.np / sp.ne;
-      n_items = sp.p_lo + (e + 1) * sp.np / sp.ne - p0;
-      tail = 1;
-    }
-  }
+  const AttendWork wk = attend_work(pairs, a.part != nullptr, a.sched, a.slots_x, a.cut_max,
+                                    gridDim.x, blockIdx.x);
+  if (wk.n_items < 0) return;  // padding: XCDs with fewer pairs
+  const int p0 = wk.p0, n_items = wk.n_items, k = wk.k, tail = wk.tail, slot0 = wk.slot0;
   const int64_t rs_bytes = (a.tok_off ? (int64_t)kD : a.kv_row_stride) * 2;
 
   // Staging: wave w fills tile rows 16 w .. 16 w + 15, four rows per
@@ -610,13 +538,13 @@ size_t attend_part_bytes() {
   return (size_t)2 * 2 * device_cus() * kPartFloats * sizeof(float);
 }
 
-// Schedule of a bf16 attention launch over all heads (the sched field): 1
-// (split) with a partial-result buffer and at most one pair per CU; 2
-// (rounds) with one and more pairs than resident workgroups when some pairs
-// are left for a last round; else 0, one workgroup per pair.  Fills the
-// schedule fields of a and returns the combine kernel's workgroups (0: none).
-namespace {
-int plan_attend_bf16(AttendArgs &a, void *part, size_t part_bytes) {
+// Schedule of an attention launch over all heads (the sched field; the bf16
+// and the fp8 kernel both run two workgroups per CU): 1 (split) with a
+// partial-result buffer and at most one pair per CU; 2 (rounds) with one and
+// more pairs than resident workgroups when some pairs are left for a last
+// round; else 0, one workgroup per pair.  Fills the schedule fields of a and
+// returns the combine kernel's workgroups (0: none).
+int plan_attend(AttendArgs &a, void *part, size_t part_bytes) {
   const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
   // Two workgroups fit on a CU (64 KiB of LDS each).  The split schedule
   // runs exactly that many, all resident at once, when there is at most one
@@ -656,11 +584,16 @@ int plan_attend_bf16(AttendArgs &a, void *part, size_t part_bytes) {
   }
   return 0;
 }
-}  // namespace
+
+hipError_t launch_attend_combine(const AttendArgs &a, int blocks, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 int attend_bf16_schedule(const AttendArgs &a0, void *part, size_t part_bytes) {
   AttendArgs a = a0;
-  plan_attend_bf16(a, part, part_bytes);
+  plan_attend(a, part, part_bytes);
   return a.sched;
 }
 
@@ -668,7 +601,7 @@ hipError_t launch_attend_bf16(const AttendArgs &a0, void *part, size_t part_byte
                               hipStream_t s) {
   if (a0.D != kD) return hipErrorInvalidValue;
   AttendArgs a = a0;
-  const int combine_blocks = plan_attend_bf16(a, part, part_bytes);
+  const int combine_blocks = plan_attend(a, part, part_bytes);
   hipLaunchKernelGGL(attend_bf16_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
   if (combine_blocks > 0)
     hipLaunchKernelGGL(attend_combine_kernel, dim3(combine_blocks), dim3(256), 0, s, a);

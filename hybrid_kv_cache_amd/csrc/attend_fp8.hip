@@ -22,6 +22,7 @@
 // weight 2^(s c - m) stays at most 2^8, inside e4m3's range.
 #include "fkv_device.h"
 #include "fkv_fp8.h"
+#include "fkv_launch.h"
 
 #include <type_traits>
 
@@ -37,6 +38,7 @@ constexpr int kBM = 128;
 constexpr int kRow = 128;                 // bytes per fp8 row
 constexpr int kTileBytes = kKT * kRow;    // 8 KiB
 constexpr float kE4m3Max = 448.f;
+constexpr int kPartFloats = kBM * kD + 2 * kBM;  // one partial-result slot (as bf16)
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -75,67 +77,26 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int ntq = (a.n_q + kBM - 1) / kBM;
-  int h, qt;
-  {
-    // XCD-aware order: workgroup b runs on XCD b % 8, each XCD a contiguous
-    // run of (head, query tile) pairs.
-    const int nb = gridDim.x, b = blockIdx.x, x = b & 7;
-    const int pair = x * (nb >> 3) + min(x, nb & 7) + (b >> 3);
-    h = pair / ntq;
-    qt = pair - h * ntq;
-  }
-  const int qi = qt * kBM + wave * 32 + col;
-  const int64_t lo = a.tok_off[h], len64 = a.tok_off[h + 1] - lo;
-  const int len = (int)len64;
-  const int ntiles = (len + kKT - 1) / kKT;
-  const float c = a.c * a.q_scale[h] * a.k_scale[h];
-
-  // Query fragments: lane (query, g) holds dims 64 ds + 32 g + 0 .. 31 as
-  // e4m3 codes of q / q_scale.
-  i32x8 qf[2];
-  {
-    const float qs = a.q_scale[h];
-#pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      qf[ds] = i32x8{};
-      if (qi < a.n_q) {
-        const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
-                           ((int64_t)qi * a.H + h) * kD + 64 * ds + 32 * g;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          float f[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = clamp448((float)qp[4 * w + e] / qs);
-          int v = cvt2<false>(f[0], f[1], 0);
-          v = cvt2<true>(f[2], f[3], v);
-          qf[ds][w] = v;
-        }
-      }
-    }
-  }
+  // Work: (head, 128-query tile) pairs p = h * ntq + qt, each XCD (workgroup
+  // b runs on XCD b % 8) a contiguous run of them; with a partial-result
+  // buffer the balanced schedules of the bf16 kernel (attend_work): pairs
+  // cut into a main part and a tail, or the last round's pairs halved,
+  // their partial results merged by the combine kernel.
+  const AttendWork wk = attend_work(ntq * a.H, a.part != nullptr, a.sched, a.slots_x, a.cut_max,
+                                    gridDim.x, blockIdx.x);
+  if (wk.n_items < 0) return;  // padding: XCDs with fewer pairs
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   // Staging: wave w copies tile rows 16 w .. 16 w + 15, 8 rows per
   // instruction; lane i lands at row 16 w + 8 j + i / 8, chunk position i % 8,
   // fetching global chunk (i % 8) ^ swz8(row).  The buffer resource ends at
   // the head's last row (rows past it read as zeros).
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const char *kbase_g = reinterpret_cast<const char *>(a.k) + lo * kRow;
-  const char *vbase_g = reinterpret_cast<const char *>(a.v) + lo * kRow;
-  const uint32_t range_bytes = (uint32_t)(len64 * kRow);
-  const buf_rsrc krsrc = make_rsrc(kbase_g, range_bytes);
-  const buf_rsrc vrsrc = make_rsrc(vbase_g, range_bytes);
   uint32_t goff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 16 * wave + 8 * j + (lane >> 3);
     goff[j] = (uint32_t)row * kRow + (((lane & 7) ^ swz8(row)) << 4) - 1024u * j;
   }
-  auto issue = [&](const buf_rsrc &rsrc, int it, char *dst) {
-    const uint32_t soff = (uint32_t)(it * kKT * kRow);
-    char *dw = dst + wave_s * 2048;
-    buffer_load_lds16<0>(rsrc, goff[0], soff, dw);
-    buffer_load_lds16<1024>(rsrc, goff[1], soff, dw);
-  };
 
   // K fragment addresses: A lane (row R = 32 kb + col, g) reads key
   // sigma(R) = 32 ((R >> 2) & 1) + 16 kb + 4 ((R >> 3) & 3) + (R & 3),
@@ -167,6 +128,54 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) ones[w] = col == 0 ? 0x38383838 : 0;
 
+  for (int item = 0; item < wk.n_items; ++item) {
+  const int p = wk.p0 + item;
+  const int h = p / ntq, qt = p - h * ntq;
+  const int qi = qt * kBM + wave * 32 + col;
+  const int64_t lo = a.tok_off[h], len64 = a.tok_off[h + 1] - lo;
+  const int len = (int)len64;
+  const int nt = (len + kKT - 1) / kKT;
+  const int ts = wk.k < 0 ? nt / 2 : split_tile(nt, wk.k);
+  const int t0 = wk.tail ? ts : 0, t1 = wk.tail ? nt : ts;
+  if (t0 >= t1) continue;
+  const float c = a.c * a.q_scale[h] * a.k_scale[h];
+
+  // Query fragments: lane (query, g) holds dims 64 ds + 32 g + 0 .. 31 as
+  // e4m3 codes of q / q_scale.
+  i32x8 qf[2];
+  {
+    const float qs = a.q_scale[h];
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      qf[ds] = i32x8{};
+      if (qi < a.n_q) {
+        const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
+                           ((int64_t)qi * a.H + h) * kD + 64 * ds + 32 * g;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = clamp448((float)qp[4 * w + e] / qs);
+          int v = cvt2<false>(f[0], f[1], 0);
+          v = cvt2<true>(f[2], f[3], v);
+          qf[ds][w] = v;
+        }
+      }
+    }
+  }
+
+  const char *kbase_g = reinterpret_cast<const char *>(a.k) + lo * kRow;
+  const char *vbase_g = reinterpret_cast<const char *>(a.v) + lo * kRow;
+  const uint32_t range_bytes = (uint32_t)(len64 * kRow);
+  const buf_rsrc krsrc = make_rsrc(kbase_g, range_bytes);
+  const buf_rsrc vrsrc = make_rsrc(vbase_g, range_bytes);
+  auto issue = [&](const buf_rsrc &rsrc, int it, char *dst) {
+    const uint32_t soff = (uint32_t)(it * kKT * kRow);
+    char *dw = dst + wave_s * 2048;
+    buffer_load_lds16<0>(rsrc, goff[0], soff, dw);
+    buffer_load_lds16<1024>(rsrc, goff[1], soff, dw);
+  };
+
   auto qk = [&](const char *kl, f32x16 *sacc) {
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -196,8 +205,8 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
     char *const v_fill = P ? sv0 : sv1;     // V(it+1)
     wait_vmcnt0();
     lds_barrier();
-    if (it + 2 < ntiles) issue(krsrc, it + 2, k_fill);
-    if (it + 1 < ntiles) issue(vrsrc, it + 1, v_fill);
+    if (it + 2 < t1) issue(krsrc, it + 2, k_fill);
+    if (it + 1 < t1) issue(vrsrc, it + 1, v_fill);
     const int valid = len - it * kKT;
     if (valid < kKT) {
       // The lane's part of the key index (32 g) moves to the bound, so each
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
     mx = pair_max(mx) * c;
-    if (it == 0) {
+    if (it == t0) {
       m = mx;
     } else if (__any(mx > m + 8.f)) {
       const float mnew = fmaxf(m, mx);
@@ -278,39 +287,67 @@ __global__ __launch_bounds__(256, 2) void attend_fp8_kernel(AttendFp8Args a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
-  if (ntiles > 0) {
-    issue(krsrc, 0, sk0);
-    issue(vrsrc, 0, sv0);
-    if (ntiles > 1) issue(krsrc, 1, sk1);
+  {
+    issue(krsrc, t0, sk0);
+    issue(vrsrc, t0, sv0);
+    if (t0 + 1 < t1) issue(krsrc, t0 + 1, sk1);
     wait_vmcnt0();
     lds_barrier();
     f32x16 sa[2], sb[2];
     qk(sk0, sa);
-    int it = 0;
-    for (; it + 1 < ntiles; it += 2) {
+    int it = t0;
+    for (; it + 1 < t1; it += 2) {
       step(std::integral_constant<int, 0>{}, it, sa, sb);
       step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
     }
-    if (it < ntiles) step(std::integral_constant<int, 0>{}, it, sa, sb);
+    if (it < t1) step(std::integral_constant<int, 0>{}, it, sa, sb);
   }
 
   // Row sums sit in element 0 of the g = 0 lane of each query.
   const float l0 = lsum[0];
   const float l1 = swap_halves(l0);
   const float l = g == 0 ? l0 : l1;
-  const float f = a.v_scale[h] / l;
-  if (qi < a.n_q) {
-    __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
+  if (t0 == 0 && t1 == nt) {
+    // Whole pair: normalise and store.
+    const float f = a.v_scale[h] / l;
+    if (qi < a.n_q) {
+      __bf16 *op = reinterpret_cast<__bf16 *>(a.out) + ((int64_t)qi * a.H + h) * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = db * 32 + 8 * rr + 4 * g;
+          bf16x2 p2 = pack_bf16(o[db][4 * rr] * f, o[db][4 * rr + 1] * f);
+          bf16x2 q2 = pack_bf16(o[db][4 * rr + 2] * f, o[db][4 * rr + 3] * f);
+          u32x2 w = {__builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, q2)};
+          *reinterpret_cast<u32x2 *>(op + d0) = w;
+        }
+    }
+  } else {
+    // Part of a pair: O times the head's V scale (so that the combine
+    // kernel's merge gives the output directly), m and l into slot 2 p + tail
+    // (split) or slot0 + tail (halves), in the layout of the bf16 kernel.
+    float *slot = a.part + (int64_t)((wk.slot0 >= 0 ? wk.slot0 : 2 * p) + wk.tail) * kPartFloats;
+    const int ql = wave * 32 + col;
+    const float vs = a.v_scale[h];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = db * 32 + 8 * rr + 4 * g;
-        bf16x2 p = pack_bf16(o[db][4 * rr] * f, o[db][4 * rr + 1] * f);
-        bf16x2 q = pack_bf16(o[db][4 * rr + 2] * f, o[db][4 * rr + 3] * f);
-        u32x2 w = {__builtin_bit_cast(uint32_t, p), __builtin_bit_cast(uint32_t, q)};
-        *reinterpret_cast<u32x2 *>(op + d0) = w;
+        f32x4 w = {o[db][4 * rr] * vs, o[db][4 * rr + 1] * vs, o[db][4 * rr + 2] * vs,
+                   o[db][4 * rr + 3] * vs};
+        *reinterpret_cast<f32x4 *>(slot + ql * kD + d0) = w;
       }
+    if (g == 0) {
+      slot[kBM * kD + ql] = m;
+      slot[kBM * kD + kBM + ql] = l;
+    }
+  }
+
+  // The next item refills the LDS tiles: every wave must be done with
+  // this one's.
+  lds_barrier();
   }
 }
 
@@ -378,10 +415,27 @@ __global__ __launch_bounds__(256) void compact_fp8_fixed_kernel(FixedCopyPlan p,
 
 }  // namespace
 
-hipError_t launch_attend_fp8(const AttendFp8Args &a, hipStream_t s) {
-  const int pairs = ((a.n_q + kBM - 1) / kBM) * a.H;
-  hipLaunchKernelGGL(attend_fp8_kernel, dim3(pairs), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_attend_fp8(const AttendFp8Args &a0, void *part, size_t part_bytes,
+                             hipStream_t s) {
+  // The bf16 planner and combine kernel serve as they are: same pairs, tiles
+  // of 64 keys, two workgroups per CU and partial-result layout.
+  AttendArgs c = {};
+  c.out = a0.out;
+  c.tok_off = a0.tok_off;
+  c.n_q = a0.n_q;
+  c.H = a0.H;
+  c.D = kD;
+  const int combine_blocks = plan_attend(c, part, part_bytes);
+  AttendFp8Args a = a0;
+  a.part = c.part;
+  a.n_wg = c.n_wg;
+  a.sched = c.sched;
+  a.slots_x = c.slots_x;
+  a.cut_max = c.cut_max;
+  hipLaunchKernelGGL(attend_fp8_kernel, dim3(a.n_wg), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_attend_combine(c, combine_blocks, s);
+  return e;
 }
 
 hipError_t launch_compact_fp8_fixed(const FixedCopyPlan &p, const Fp8Scales &sc, hipStream_t s) {

@@ -290,4 +290,99 @@ __device__ __forceinline__ CopySlot fixed_slot(const FixedCopyPlan &p, int s) {
   return sl;
 }
 
+// ---- attention schedules (bf16 and fp8 kernels, and their launchers) ----
+//
+// Split schedule on XCD x (nb workgroups, nb % 8 == 0, at most nb / 2
+// pairs): the XCD's pairs are [p_lo, p_lo + np) and its workgroups
+// xs = 0 .. nb/8 - 1.  The first np workgroups run tiles [0, split) of one
+// pair each (main parts), the ne others the tails [split, tiles) of up to
+// k = ceil(np / ne) pairs each (k = 0: no cut).
+struct XcdSplit {
+  int p_lo, np, ne, k;
+};
+__host__ __device__ __forceinline__ XcdSplit xcd_split(int pairs, int nb, int x) {
+  XcdSplit s;
+  s.p_lo = pairs * x / 8;
+  s.np = pairs * (x + 1) / 8 - s.p_lo;
+  s.ne = nb / 8 - s.np;
+  s.k = s.ne > 0 ? (s.np + s.ne - 1) / s.ne : 0;
+  return s;
+}
+// Rounds schedule on XCD x (more pairs than resident workgroups): the XCD's
+// pairs are [p_lo, p_lo + np) and slots_x workgroups of it run at a time.
+// The first w pairs run whole, one workgroup each, in full rounds plus part
+// of the last; the s pairs after them are cut in two halves (tiles
+// [0, nt/2) and [nt/2, nt)) so that the last round is full too: with
+// rem = np mod slots_x, s = rem when 2 rem <= slots_x (the last round is
+// halves only), else s = slots_x - rem (rem - s whole pairs and 2 s halves).
+struct XcdRounds {
+  int p_lo, np, w, s;
+};
+__host__ __device__ __forceinline__ XcdRounds xcd_rounds(int pairs, int slots_x, int x) {
+  XcdRounds r;
+  r.p_lo = pairs * x / 8;
+  r.np = pairs * (x + 1) / 8 - r.p_lo;
+  const int rem = r.np % slots_x;
+  r.s = rem == 0 ? 0 : (2 * rem <= slots_x ? rem : slots_x - rem);
+  r.w = r.np - r.s;
+  return r;
+}
+
+// First tail tile of a pair with nt tiles (nt when nothing is cut).  A
+// tail workgroup runs its k tails one after the other, each restarting the
+// copy pipeline, and takes about 9/8 the time per tile of a main workgroup;
+// split = nt * 9k / (8 + 9k) evens out the two.
+__host__ __device__ __forceinline__ int split_tile(int nt, int k) {
+  return k > 0 ? (int)((int64_t)nt * (9 * k) / (8 + 9 * k)) : nt;
+}
+
+// What one workgroup of an attention launch does: n_items pairs p0, p0 + 1,
+// ... (tail parts of the split schedule: one each), cut as k says (0: whole
+// pairs, > 0: split_tile(nt, k), -1: halves), the tail part when tail is 1,
+// partial results in slot0 (halves) or 2 p + tail (split).  n_items < 0:
+// nothing (padding of the rounds schedule).  Without a partial-result
+// buffer every workgroup takes one whole pair, each XCD (workgroup b runs on
+// XCD b % 8) a contiguous run of them.
+struct AttendWork {
+  int p0, n_items, k, tail, slot0;
+};
+__device__ __forceinline__ AttendWork attend_work(int pairs, bool has_part, int sched,
+                                                  int slots_x, int cut_max, int nb, int b) {
+  const int x = b & 7, xs = b >> 3;
+  AttendWork w;
+  w.k = 0;
+  w.tail = 0;
+  w.slot0 = -1;
+  w.n_items = 1;
+  if (!has_part) {
+    w.p0 = x * (nb >> 3) + min(x, nb & 7) + xs;
+  } else if (sched == 2) {
+    const XcdRounds xr = xcd_rounds(pairs, slots_x, x);
+    if (xs < xr.w) {
+      w.p0 = xr.p_lo + xs;
+    } else if (xs < xr.w + 2 * xr.s) {
+      const int c = (xs - xr.w) >> 1;
+      w.tail = (xs - xr.w) & 1;
+      w.p0 = xr.p_lo + xr.w + c;
+      w.k = -1;  // halves
+      w.slot0 = 2 * (x * cut_max + c);
+    } else {
+      w.p0 = 0;
+      w.n_items = -1;
+    }
+  } else {
+    const XcdSplit sp = xcd_split(pairs, nb, x);
+    w.k = sp.k;
+    if (xs < sp.np) {
+      w.p0 = sp.p_lo + xs;
+    } else {
+      const int e = xs - sp.np;
+      w.p0 = sp.p_lo + e * sp.np / sp.ne;
+      w.n_items = sp.p_lo + (e + 1) * sp.np / sp.ne - w.p0;
+      w.tail = 1;
+    }
+  }
+  return w;
+}
+
 }  // namespace fkv

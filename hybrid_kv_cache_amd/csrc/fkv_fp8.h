@@ -42,11 +42,17 @@ struct AttendFp8Args {
   float q_scale[kMaxHeads];
   float k_scale[kMaxHeads];
   float v_scale[kMaxHeads];
+  // Schedule (set by launch_attend_fp8, as for the bf16 kernel).
+  float *part;              // partial-result slots or null
+  int32_t n_wg, sched, slots_x, cut_max;
 };
 
 hipError_t launch_compact_fp8(const CompactFp8Args &a, int total_slots, hipStream_t s);
 // The quantizing copies of the fixed compaction jobs of p.
 hipError_t launch_compact_fp8_fixed(const FixedCopyPlan &p, const Fp8Scales &sc, hipStream_t s);
-hipError_t launch_attend_fp8(const AttendFp8Args &a, hipStream_t s);
+// part / part_bytes: the bf16 attention's partial-result buffer
+// (attend_part_bytes()) for its balanced schedules, or null / 0 for one
+// workgroup per (head, query tile) pair.
+hipError_t launch_attend_fp8(const AttendFp8Args &a, void *part, size_t part_bytes, hipStream_t s);
 
 }  // namespace fkv

@@ -139,7 +139,7 @@ struct AttendArgs {
   int32_t dense_len;      // window length when tok_off is null
   int32_t n_q, H, D;
   float c;                // scale * log2(e)
-  float *part;            // partial-result slots (balanced bf16 schedules) or null
+  float *part;            // partial-result slots (balanced schedules) or null
   int32_t n_wg;           // workgroups of the balanced schedules
   int32_t sched;          // 0: one workgroup per pair; 1: split; 2: rounds + halves
   int32_t slots_x;        // schedule 2: resident workgroups per XCD
@@ -167,6 +167,12 @@ hipError_t launch_attend_bf16(const AttendArgs &a, void *part, size_t part_bytes
 // The schedule launch_attend_bf16 would pick (AttendArgs.sched) for a and the
 // partial-result buffer.
 int attend_bf16_schedule(const AttendArgs &a, void *part, size_t part_bytes);
+// Fills the schedule fields of a (over all a.H heads, two workgroups per CU)
+// for the partial-result buffer, null for one workgroup per pair; returns the
+// combine kernel's workgroups (0: none).  launch_attend_combine merges the
+// partial results of a launch planned so into a.out (bf16).
+int plan_attend(AttendArgs &a, void *part, size_t part_bytes);
+hipError_t launch_attend_combine(const AttendArgs &a, int blocks, hipStream_t s);
 // The heads a.sel[0 .. a.n_sel) of the ragged cache, one workgroup per pair.
 hipError_t launch_attend_bf16_heads(const AttendArgs &a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs &a, hipStream_t s);

@@ -97,7 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, P, P, ctypes.POINTER(FkvCkv), P, P, SZ, P]
     lib.fkv_compress_fp8.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, P, I32, P,
                                      ctypes.POINTER(FkvCkv), P, SZ, P]
-    lib.fkv_attend_fp8.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, P]
+    lib.fkv_attend_fp8.argtypes = [ctypes.POINTER(FkvDesc), P, ctypes.POINTER(FkvCkv), P, P, P, SZ,
+                                   P]
     lib.fkv_profile_workspace.argtypes = [ctypes.POINTER(FkvDesc), ctypes.POINTER(SZ)]
     lib.fkv_profile_heads.argtypes = [ctypes.POINTER(FkvDesc), P, P, P, P, SZ, P]
     lib.fkv_classify_heads.argtypes = [ctypes.POINTER(FkvDesc), P, I32, ctypes.c_float, P, P, P]
@@ -343,12 +344,14 @@ def fkv_compress_fp8(desc: FkvDesc, q, k_cache, v_cache, head_role, static_keep_
 
 
 def fkv_attend_fp8(desc: FkvDesc, q, ckv: CompressedKV, q_scale, k_scale, v_scale, out,
-                   stream=None) -> None:
+                   workspace="ckv", stream=None) -> None:
+    """workspace: as for fkv_attend ("ckv", None or a device buffer)."""
     lib = load()
     sc = _host_f32(np.concatenate([np.ravel(q_scale), np.ravel(k_scale), np.ravel(v_scale)]))
     s = ckv.struct()
+    ws, ws_bytes = _ws(ckv.attend_ws if isinstance(workspace, str) else workspace)
     _check(lib.fkv_attend_fp8(ctypes.byref(desc), _ptr(q), ctypes.byref(s), sc.ctypes.data,
-                              _ptr(out), _stream(stream)))
+                              _ptr(out), ws, ws_bytes, _stream(stream)))
 
 
 def fkv_profile_workspace(desc: FkvDesc) -> int:

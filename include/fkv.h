@@ -247,9 +247,16 @@ fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void 
  * scale * (q_hat . k_hat) * q_scale * k_scale, outputs sum_j p_j v_hat_j *
  * v_scale / sum_j p_j with the weights p_j themselves rounded to e4m3 for
  * the value product (the sums use the same rounded weights).  scales: host
- * [3 H]: Q, K, V scales per head.  out as for fkv_attend (bf16). */
+ * [3 H]: Q, K, V scales per head.  out as for fkv_attend (bf16).
+ * workspace / workspace_bytes: optional, as for fkv_attend and of the same
+ * size (fkv_attend_workspace of a bf16 descriptor): with it the launch takes
+ * the same balanced schedules (pairs cut where that evens out the CUs, the
+ * parts merged by a second kernel); NULL / 0: one workgroup per (head,
+ * 128-query tile).  Calls that share a workspace must be ordered on one
+ * stream.  The desc dtype must be FKV_BF16 (else FKV_ERR_DTYPE). */
 fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv_t *ckv,
-                            const float *scales, void *out, void *stream);
+                            const float *scales, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* ---- Token-granular variant ----------------------------------------------
  * Static heads keep positions at token granularity ([S] 关键模块 1 and 2:

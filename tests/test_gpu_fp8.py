@@ -1,5 +1,7 @@
 """GPU parity of the FP8 (OCP e4m3) compressed cache: quantizing compaction
-(bit-exact codes) and fp8 attention against the CPU oracle."""
+(bit-exact codes) and fp8 attention against the CPU oracle, with and without
+the attention workspace (one workgroup per pair, or the balanced schedules:
+pairs cut into a main part and a tail, or the last round's pairs halved)."""
 import numpy as np
 import pytest
 
@@ -28,7 +30,7 @@ def head_scales(a, H, D):
     return np.maximum(x, 1e-6).astype(np.float32) / np.float32(448.0)
 
 
-def run_fp8(w, inp, rows=None, check_codes=True):
+def run_fp8(w, inp, rows=None, check_codes=True, workspace="ckv"):
     import torch
     H, D, T, Fh, Fc = w.num_heads, w.head_dim, w.tokens_per_frame, w.hist_frames, w.cur_frames
     ks, vs, qs = head_scales(inp.k, H, D), head_scales(inp.v, H, D), head_scales(inp.q, H, D)
@@ -49,8 +51,8 @@ def run_fp8(w, inp, rows=None, check_codes=True):
         assert np.array_equal(k8, ref["k8"]), "K codes differ"
         assert np.array_equal(v8, ref["v8"]), "V codes differ"
     out = torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda")
-    G.announce(f"fkv_attend_fp8 {w.name} rows={n}")
-    fkv.fkv_attend_fp8(desc, q, ckv, qs, ks, vs, out)
+    G.announce(f"fkv_attend_fp8 {w.name} rows={n} workspace={workspace}")
+    fkv.fkv_attend_fp8(desc, q, ckv, qs, ks, vs, out, workspace)
     torch.cuda.synchronize()
     got = G.host_f64(out)
     if rows is not None:
@@ -60,15 +62,17 @@ def run_fp8(w, inp, rows=None, check_codes=True):
     return err, got, want
 
 
+@pytest.mark.parametrize("ws", [None, "ckv"])
 @pytest.mark.parametrize("T,H,Fh,s,m,nst,seed", [
     (100, 3, 6, 4, 4, 1, 51),      # ragged tiles
     (64, 2, 6, 1, 3, 0, 52),       # exact tiles, all dynamic
     (130, 4, 18, 16, 13, 2, 53),   # 18 history frames
 ])
-def test_fp8_codes_and_attention(T, H, Fh, s, m, nst, seed):
+def test_fp8_codes_and_attention(T, H, Fh, s, m, nst, seed, ws):
+    """With the workspace these few pairs take the split schedule."""
     w = W.small_workload(tokens_per_frame=T, num_heads=H, hist_frames=Fh, query_stride=s,
                          budget_m=m, num_static=nst, seed=seed)
-    err, _, _ = run_fp8(w, W.generate_layer(w))
+    err, _, _ = run_fp8(w, W.generate_layer(w), workspace=ws)
     assert err.max() <= FP8_MAX_ABS, err.max()
     assert err.mean() <= FP8_MEAN_ABS, err.mean()
 
@@ -98,6 +102,25 @@ def test_fp8_late_large_scores_raise_the_reference():
     inp.k = W.round_to_bf16_bits(kf)
     err, _, _ = run_fp8(w, inp)
     assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("T,H,Fh,seed", [
+    (2000, 12, 1, 57),    # 564 pairs: 70-71 per XCD, the last 6-7 halved
+    (2731, 13, 1, 58),    # 845 pairs: 22-23 halved per XCD
+])
+def test_fp8_rounds_schedule(T, H, Fh, seed):
+    """More (head, query tile) pairs than resident workgroups: with the
+    workspace whole pairs run in rounds and the last round's pairs are
+    halved, each half with its own reference, merged by the combine kernel
+    (which takes the halves' outputs already times the V scale)."""
+    w = W.small_workload(tokens_per_frame=T, num_heads=H, hist_frames=Fh, budget_m=Fh,
+                         num_static=0, query_stride=7, seed=seed)
+    inp = W.generate_layer(w)
+    rows = np.random.default_rng(seed).choice(w.n_q, 48, replace=False)
+    rows[0], rows[-1] = 0, w.n_q - 1
+    for ws in ("ckv", None):
+        err, _, _ = run_fp8(w, inp, rows=rows, check_codes=ws == "ckv", workspace=ws)
+        assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS, (ws, err.max(), err.mean())
 
 
 def test_fp8_480p_layer():
