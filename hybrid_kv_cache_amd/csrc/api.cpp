@@ -749,7 +749,6 @@ fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv
                             size_t workspace_bytes, void *stream) {
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;
-  if (desc->dtype != FKV_BF16) return fail(FKV_ERR_DTYPE, "the fp8 attention takes bf16 queries");
   st = check_scales(desc, scales, 3 * desc->num_heads, "scales");
   if (st != FKV_OK) return st;
   if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");

@@ -241,6 +241,29 @@ def test_attend_argument_errors(lib):
     assert lib.fkv_attend_dense(ctypes.byref(d), 1, 1, 1, 1, None, 0, None) == fkv.FKV_ERR_DTYPE
 
 
+def test_attend_fp8_argument_errors(lib):
+    """fkv_attend_fp8 rejects, on the host: a missing cache or query, missing
+    or non-positive scales, and a non-bf16 descriptor."""
+    import numpy as np
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    good = np.ones(3 * 2, dtype=np.float32)
+    ckv = fkv.FkvCkv(None, None, None, None, None, None, 0)
+    assert lib.fkv_attend_fp8(ctypes.byref(d), 0x1000, ctypes.byref(ckv), good.ctypes.data,
+                              0x1000, None, 0, None) == fkv.FKV_ERR_NULL
+    full = fkv.FkvCkv(0x1000, 0x1000, 0x1000, None, None, None, 0)
+    assert lib.fkv_attend_fp8(ctypes.byref(d), None, ctypes.byref(full), good.ctypes.data,
+                              0x1000, None, 0, None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_attend_fp8(ctypes.byref(d), 0x1000, ctypes.byref(full), None, 0x1000, None,
+                              0, None) != fkv.FKV_OK
+    bad = good.copy()
+    bad[4] = 0.0
+    assert lib.fkv_attend_fp8(ctypes.byref(d), 0x1000, ctypes.byref(full), bad.ctypes.data,
+                              0x1000, None, 0, None) != fkv.FKV_OK
+    d32 = fkv.make_desc(2, 128, 16, 4, 3, 4, dtype="f32")
+    assert lib.fkv_attend_fp8(ctypes.byref(d32), 0x1000, ctypes.byref(full), good.ctypes.data,
+                              0x1000, None, 0, None) == fkv.FKV_ERR_DTYPE
+
+
 def test_attend_workspace_query(lib):
     """The workspace figure: NULL output rejected, bad descriptors rejected,
     0 for fp32 (no balanced schedule there), and for bf16 either a positive
