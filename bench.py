@@ -292,6 +292,7 @@ def measure_rolling(wname, args, fkv, torch, W, n_chunks=8):
         fkv.fkv_refresh_current(desc, cur_k, cur_v, out_ckv)
         fkv.fkv_attend(desc, q, out_ckv, out, hist.attend_ws)
 
+    clock_warmup(chunk_step, [None], args.clock_warmup, torch)
     ms_chunk = time_loop(chunk_step, [None], args.steps, args.warmup, torch)
     ms_reuse = time_loop(reuse_step, [None], args.steps, args.warmup, torch)
     rows, _ = fkv.fkv_plan_ragged(desc, hist_frames, ro.head_role, mask, w.budget_m)
@@ -329,6 +330,7 @@ def measure_tokens(wname, args, fkv, torch, W):
         compress(None)
         fkv.fkv_attend(L.desc, L.q, ckv, L.out)
 
+    clock_warmup(step, [None], args.clock_warmup, torch)
     ms_c = time_loop(compress, [None], args.steps, args.warmup, torch)
     ms_s = time_loop(step, [None], args.steps, args.warmup, torch)
     return {"workload": w.name,
@@ -366,6 +368,7 @@ def measure_fp8(wname, args, fkv, torch, W):
         attend(None)
 
     steps = args.steps if w.tokens_per_frame < 5000 else max(args.steps // 4, 3)
+    clock_warmup(step, [None], args.clock_warmup, torch)
     ms_s = time_loop(step, [None], steps, args.warmup, torch)
     ms_c = time_loop(compress, [None], steps, args.warmup, torch)
     ms_a = time_loop(attend, [None], steps, args.warmup, torch)
