@@ -327,18 +327,18 @@ fkv_status_t fkv_classify_heads(const fkv_desc_t *desc, const float *mass_sum, i
 
 /* Attention workspace.  The method's attention call takes only the queries
  * and the compressed cache; the (workspace, workspace_bytes) pair of
- * fkv_attend and fkv_attend_dense is an addition of this library, optional
- * (NULL, 0 is always accepted) and used only to balance the work of a
- * launch across the compute units.
+ * fkv_attend, fkv_attend_dense and fkv_attend_fp8 is an addition of this
+ * library, optional (NULL, 0 is always accepted) and used only to balance
+ * the work of a launch across the compute units.
  *
  * Bytes of the optional attention workspace for the current HIP device: with
- * it the bf16 attention balances its (head, 128-query) tiles over the
- * resident workgroups (two per compute unit): with at most one tile per
- * compute unit it cuts tiles into a main part and tails; with more tiles
- * than resident workgroups it runs whole tiles in rounds and halves those
- * left for the last round so that it is full.  The pieces of cut tiles are
- * merged from partial results kept in the workspace.  0 for fp32.
- * FKV_ERR_HIP when no device is visible. */
+ * it the bf16 attention (and the fp8 attention, which takes the same size)
+ * balances its (head, 128-query) tiles over the resident workgroups (two per
+ * compute unit): with at most one tile per compute unit it cuts tiles into a
+ * main part and tails; with more tiles than resident workgroups it runs
+ * whole tiles in rounds and halves those left for the last round so that it
+ * is full.  The pieces of cut tiles are merged from partial results kept in
+ * the workspace.  0 for fp32.  FKV_ERR_HIP when no device is visible. */
 fkv_status_t fkv_attend_workspace(const fkv_desc_t *desc, size_t *workspace_bytes);
 
 /* Attention of the whole query block over the compressed cache ([S]
