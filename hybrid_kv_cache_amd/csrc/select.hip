@@ -17,10 +17,11 @@
 // thread at a time, the softmax over its frames in registers, masses summed
 // per thread, then over each wave and over the waves in a fixed order
 // (deterministic).
-// Wave 0 then sorts the (score, frame) pairs with a 64-lane bitonic network
-// (lane exchanges by DPP and permlane swaps, not the LDS crossbar) and marks
-// the first m_eff.  Every head finally writes its seg_idx entries (bit rank =
-// position), its offsets and its compaction slots.
+// Wave 0 then ranks the frames (lane f counts the frames whose (score,
+// index) pair ranks before its own, reading them by readlane) and keeps those
+// of rank below m_eff, a ballot giving the kept-frame bit mask.  Every head
+// finally writes its seg_idx entries (bit rank = position), its offsets and
+// its compaction slots.
 #include "fkv_device.h"
 #include "fkv_launch.h"
 
@@ -48,37 +49,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, r32.a) + __builtin_bit_cast(float, r32.b);
 }
 
-// The value of lane `lane ^ j` (j a power of two below 64; the loops that
-// call it are unrolled, so j is a constant there): xor 1 and 2 by DPP quad
-// permutes, xor 4 and 8 by DPP row shifts (lanes with the bit clear take the
-// lane j above, the others the lane j below, always inside the row of 16),
-// xor 16 and 32 by the permlane swaps of rows and halves.
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j, int lane) {
-  const int x = (int)v;
-  switch (j) {
-    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
-    case 4: {
-      const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);   // row_shl:4
-      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-      return (uint32_t)((lane & 4) ? dn : up);
-    }
-    case 8: {
-      const int up = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0xF, false);   // row_shl:8
-      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-      return (uint32_t)((lane & 8) ? dn : up);
-    }
-    case 16: {
-      const LanePair r = permlane16_swap_copies(v);   // rows [0,0,2,2] / [1,1,3,3]
-      return (lane & 16) ? r.a : r.b;
-    }
-    default: {
-      const LanePair r = permlane32_swap_copies(v);   // halves [lo,lo] / [hi,hi]
-      return (lane & 32) ? r.a : r.b;
-    }
-  }
-}
-
 // (score, idx) a ranks before b: higher score first, then lower index.
 __device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
@@ -103,6 +73,11 @@ template <int FT, int W>
 __device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int ft,
                                                   int fh, float (*part)[kPartFrames], int tid,
                                                   int lane, int wave) {
+  if (wave * 64 >= n_s) {
+    // No sampled query reaches this wave: its partial sums are 0.
+    if (lane < fh && lane < kPartFrames) part[wave][lane] = 0.f;
+    return;
+  }
   float acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = 0.f;
@@ -175,38 +150,20 @@ __global__ __launch_bounds__(64 * W) void select_kernel(SelectArgs a) {
       } else if (a.seg_score && lane < a.F_h) {
         a.seg_score[(int64_t)h * a.F_h + lane] = __builtin_nanf("");
       }
-      // Bitonic sort of 64 (score, frame) pairs into ranking order.  A NaN
-      // score ranks like -inf, so the m_eff first entries are always real
-      // frames (lanes >= fh carry -inf and larger indices).
-      float s = score != score ? -INFINITY : score;
-      int idx = lane;
-#pragma unroll
-      for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-          const float os = __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, s), j, lane));
-          const int oi = (int)lane_xor((uint32_t)idx, j, lane);
-          const bool lower = (lane & j) == 0;
-          const bool ascending = (lane & k) == 0;
-          const bool other_first = ranks_before(os, oi, s, idx);
-          // The lower lane of an ascending pair keeps the element that ranks
-          // first; descending pairs the reverse.
-          const bool take = (lower == ascending) ? other_first : !other_first;
-          if (take) {
-            s = os;
-            idx = oi;
-          }
-        }
+      // Rank of frame `lane` among the head's fh history frames: the number
+      // of frames that rank before it (higher score, ties to the lower
+      // index; a NaN score ranks like -inf).  The ranks are a permutation
+      // of 0 .. fh - 1, and the frames of rank below m_eff are kept: the
+      // first m_eff of the ranking order, as a bit mask by frame index.
+      const float s = score != score ? -INFINITY : score;
+      int rank = 0;
+      for (int g = 0; g < fh; ++g) {
+        const float sg = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), g));
+        rank += ranks_before(sg, g, s, lane) ? 1 : 0;
       }
-      // Lane i now holds the i-th ranked frame; OR together the first m_eff.
       const int m_eff = min(a.budget, fh);
-      unsigned long long bits = lane < m_eff ? (1ull << idx) : 0ull;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t lo = lane_xor((uint32_t)bits, off, lane);
-        const uint32_t hi = lane_xor((uint32_t)(bits >> 32), off, lane);
-        bits |= ((unsigned long long)hi << 32) | lo;
-      }
+      const unsigned long long bits = __ballot(lane < fh && rank < m_eff);
       if (lane == 0) kept_bits_s = bits;
     }
   }
