@@ -97,3 +97,25 @@ def test_fp32_matches_two_calls_and_oracle():
                                         w.cur_frames)
     ref = O.attend(inp.q, k_c, v_c, tok_off)
     G.check_output(G.host_f64(out), ref, w.dtype)
+
+
+def test_random_shapes_match_two_calls():
+    """Twelve seeded random configurations (heads, frame sizes across the
+    64-row tiles, history lengths down to none, chunk sizes, strides, budgets
+    below and above F_h, mixed roles, bf16 and fp32, with and without the
+    attention workspace): one call equals the two calls bitwise."""
+    rng = np.random.default_rng(2025)
+    for case in range(12):
+        dtype = "bf16" if case % 4 else "f32"
+        Fh = int(rng.integers(0, 13))
+        w = W.small_workload(name=f"ca_sweep{case}_{dtype}", dtype=dtype,
+                             head_dim=128 if dtype == "bf16" else 64,
+                             tokens_per_frame=int(rng.integers(1, 200)),
+                             num_heads=int(rng.integers(1, 9)), hist_frames=Fh,
+                             cur_frames=int(rng.integers(1, 5)),
+                             query_stride=int(rng.integers(1, 9)),
+                             budget_m=int(rng.integers(0, Fh + 3)),
+                             num_static=0, seed=5000 + case)
+        w = W.dataclasses.replace(w, num_static=int(rng.integers(0, w.num_heads + 1)))
+        G.announce(f"one-call sweep case {case}: {w}")
+        _both(w, W.generate_layer(w), ws=None if case % 2 else "ckv")

@@ -128,3 +128,24 @@ def test_fp8_480p_layer():
     rows = np.random.default_rng(56).choice(w.n_q, 48, replace=False)
     err, _, _ = run_fp8(w, W.generate_layer(w), rows=rows)
     assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS, (err.max(), err.mean())
+
+
+def test_fp8_random_shapes():
+    """Eight seeded random configurations (heads, frame sizes across the
+    64-row tiles, history lengths down to none, strides, budgets, mixed
+    roles), with and without the attention workspace: codes bit-exact and
+    attention within the fp8 bar against the oracle."""
+    rng = np.random.default_rng(2026)
+    for case in range(8):
+        Fh = int(rng.integers(0, 13))
+        w = W.small_workload(name=f"fp8_sweep{case}", tokens_per_frame=int(rng.integers(1, 200)),
+                             num_heads=int(rng.integers(1, 9)), hist_frames=Fh,
+                             cur_frames=int(rng.integers(1, 5)),
+                             query_stride=int(rng.integers(1, 9)),
+                             budget_m=int(rng.integers(0, Fh + 3)), num_static=0,
+                             seed=6000 + case)
+        w = W.dataclasses.replace(w, num_static=int(rng.integers(0, w.num_heads + 1)))
+        G.announce(f"fp8 sweep case {case}: {w}")
+        err, _, _ = run_fp8(w, W.generate_layer(w), workspace="ckv" if case % 2 else None)
+        assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS, (case, err.max(),
+                                                                         err.mean())
