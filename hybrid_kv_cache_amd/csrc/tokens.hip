@@ -170,6 +170,25 @@ __device__ __forceinline__ void pick_digit(const int *hist, uint32_t prefix, int
   }
 }
 
+// Adds 1 to hist[bin] for every lane with take set, one LDS atomic per
+// distinct bin of the wave: the first remaining lane's bin leads, the lanes
+// with the same bin are counted by a ballot.  For the first radix pass, where
+// the keys of a wave share a few bins (sign and top exponent bits), this
+// replaces a many-way serialised atomic per lane (-10% on the whole token
+// compression at 480P); on the later passes, whose bins are spread, the
+// plain per-lane atomics are faster.
+__device__ __forceinline__ void wave_hist_add(int *hist, uint32_t bin, bool take) {
+  unsigned long long todo = __ballot(take);
+  const int lane = threadIdx.x & 63;
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const uint32_t lbin = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+    const unsigned long long same = __ballot(take && bin == lbin) & todo;
+    if (lane == leader) atomicAdd(&hist[lbin], __popcll(same));
+    todo &= ~same;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) {
   constexpr int kWaves = kSelThreads / 64;
   __shared__ uint32_t lds_keys[kLdsKeys];
@@ -226,18 +245,27 @@ __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) 
         int *mine = whist + (tid >> 6) * 256;
         const uint32_t want = prefix >> (shift + 8);
         int j = tid;
-        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {
-          uint32_t k4[4];
+        if (pass == 0) {
+          // wave-aggregated adds: the keys of a wave crowd into few bins
+          for (; j - tid < n; j += kSelThreads) {
+            const bool in = j < n;
+            const uint32_t key = in ? key_at(j) : 0u;
+            wave_hist_add(mine, (key >> shift) & 255u,
+                          in && (pass == 0 || (key >> (shift + 8)) == want));
+          }
+        } else {
+          for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {
+            uint32_t k4[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) k4[u] = key_at(j + u * kSelThreads);
+            for (int u = 0; u < 4; ++u) k4[u] = key_at(j + u * kSelThreads);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (pass == 0 || (k4[u] >> (shift + 8)) == want)
-              atomicAdd(&mine[(k4[u] >> shift) & 255u], 1);
-        }
-        for (; j < n; j += kSelThreads) {
-          const uint32_t key = key_at(j);
-          if (pass == 0 || (key >> (shift + 8)) == want) atomicAdd(&mine[(key >> shift) & 255u], 1);
+            for (int u = 0; u < 4; ++u)
+              if ((k4[u] >> (shift + 8)) == want) atomicAdd(&mine[(k4[u] >> shift) & 255u], 1);
+          }
+          for (; j < n; j += kSelThreads) {
+            const uint32_t key = key_at(j);
+            if ((key >> (shift + 8)) == want) atomicAdd(&mine[(key >> shift) & 255u], 1);
+          }
         }
         __syncthreads();
         if (tid < 256) {
