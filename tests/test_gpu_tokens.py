@@ -151,3 +151,44 @@ def test_compress_tokens_480p_shape():
     # 18,720 candidates per dynamic head; the oracle's own scores put 3 to 5
     # of them within the error bounds of the cutoff
     assert band_max <= 16
+
+
+def test_compress_tokens_candidates_beyond_lds():
+    """More candidates per dynamic head (13 frames of 2050 = 26,650) than the
+    selection stages in LDS (24,576): its radix passes then read the scores
+    from memory.  Ragged budget, boundary tokens, attention on sampled rows."""
+    w = W.small_workload(name="tokens_wide", tokens_per_frame=2050, num_heads=4, hist_frames=16,
+                         num_static=2, query_stride=11, seed=48)
+    rows = np.random.default_rng(48).choice(w.n_q, 48, replace=False)
+    rows[0], rows[-1] = 0, w.n_q - 1
+    run_tokens(w, W.generate_layer(w), fkv.FkvTokenCfg(2, 1, 5 * 2050 + 17, 300), rows=rows)
+
+
+def token_sweep_case(rng, case):
+    """One seeded random configuration of the token-variant sweep: the
+    workload and its (sink, recent, budget, boundary) configuration."""
+    dtype = "f32" if case % 4 == 3 else "bf16"
+    H, Fh = int(rng.integers(1, 9)), int(rng.integers(0, 13))
+    T = int(rng.integers(1, 200))
+    w = W.small_workload(name=f"tokens_sweep{case}", dtype=dtype,
+                         head_dim=128 if dtype == "bf16" else 64, tokens_per_frame=T,
+                         num_heads=H, hist_frames=Fh, cur_frames=int(rng.integers(1, 5)),
+                         query_stride=int(rng.integers(1, 9)), budget_m=0,
+                         num_static=int(rng.integers(0, H + 1)), seed=7000 + case)
+    S, R = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+    sink = min(S, Fh)
+    n_cand = (Fh - sink - min(R, Fh - sink)) * T
+    return w, fkv.FkvTokenCfg(S, R, int(rng.integers(0, n_cand + 6)), int(rng.integers(0, T + 3)))
+
+
+def test_compress_tokens_random_shapes():
+    """Eight seeded random configurations: head counts and roles, frame sizes
+    across the 64-row tiles, histories down to none, sink and recent zones
+    that may cover the whole history, budgets from 0 to past the candidate
+    count, boundary widths past the frame size, bf16 and fp32."""
+    rng = np.random.default_rng(2027)
+    for case in range(8):
+        w, cfg = token_sweep_case(rng, case)
+        G.announce(f"token sweep case {case}: {w} S={cfg.sink_frames} R={cfg.recent_frames} "
+                   f"C={cfg.budget_tokens} L={cfg.boundary_tokens}")
+        run_tokens(w, W.generate_layer(w), cfg)
