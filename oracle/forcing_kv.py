@@ -28,8 +28,12 @@ ranking ties broken by the lower frame index; kept frames in ascending order,
 the current chunk last; non-causal attention with scale 1/sqrt(D)).
 
 Pinned by tests/test_oracle_pins.py (invariants, closed forms, brute force,
-library cross-checks) and, for the rolling cache, tests/test_oracle_rolling.py
-(reduction to the plain window, recomputation from the frame store).  Parity of generic numeric outputs is otherwise
+library cross-checks); for the rolling cache by tests/test_oracle_rolling.py
+(reduction to the plain window, recomputation from the frame store); for the
+e4m3 cache by tests/test_oracle_fp8.py (hand-decoded codes, exactly
+representable inputs with power-of-two head scales); for the token variant by
+tests/test_oracle_tokens.py; for head profiling by
+tests/test_oracle_profile.py.  Parity of generic numeric outputs is otherwise
 pinned only through those checks; no page prints a worked example.
 
 Layouts (token-major):  q [Nq, H, D];  k, v [N_win, H, D] with the window's
