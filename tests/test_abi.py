@@ -264,6 +264,57 @@ def test_attend_fp8_argument_errors(lib):
                               0x1000, None, 0, None) == fkv.FKV_ERR_DTYPE
 
 
+
+def test_compress_fp8_timed_and_profile_argument_errors(lib):
+    """The remaining entry points reject bad arguments on the host:
+    fkv_compress_fp8 (plan errors first, then missing, zero or non-finite
+    scales, a non-bf16 descriptor, missing inputs), fkv_compress_timed (missing
+    inputs or time array), fkv_profile_workspace (NULL output; its size is
+    H x n_s x (F_h + F_c) fp32 values) and fkv_profile_heads (missing buffers,
+    a workspace below that size)."""
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    role = np.array([0, 1], np.uint8)
+    mask = np.ones((2, 4), np.uint8)
+    r, m = role.ctypes.data, mask.ctypes.data
+    ckv = fkv.FkvCkv(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0)
+    good = np.ones(2 * 2, dtype=np.float32)
+    x = 0x1000
+
+    def fp8(desc=d, q=x, m_budget=2, scales=good.ctypes.data):
+        return lib.fkv_compress_fp8(ctypes.byref(desc), q, x, x, r, m, m_budget, scales,
+                                    ctypes.byref(ckv), None, 0, None)
+    assert fp8(m_budget=-1) == fkv.FKV_ERR_BUDGET
+    assert fp8(scales=None) == fkv.FKV_ERR_NULL
+    for v in (0.0, -1.0, np.inf, np.nan):
+        bad = good.copy()
+        bad[3] = v
+        assert fp8(scales=bad.ctypes.data) == fkv.FKV_ERR_SHAPE
+        assert "kv_scales[3]" in fkv.fkv_last_error()
+    assert fp8(desc=fkv.make_desc(2, 128, 16, 4, 3, 4, dtype="f32")) == fkv.FKV_ERR_DTYPE
+    assert fp8(q=None) == fkv.FKV_ERR_NULL
+
+    ms = (ctypes.c_float * 3)()
+    assert lib.fkv_compress_timed(ctypes.byref(d), x, x, x, r, m, 2, ctypes.byref(ckv), None,
+                                  0, None, None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_compress_timed(ctypes.byref(d), None, x, x, r, m, 2, ctypes.byref(ckv), None,
+                                  0, None, ms) == fkv.FKV_ERR_NULL
+    assert lib.fkv_compress_timed(ctypes.byref(d), x, x, x, r, m, -3, ctypes.byref(ckv), None,
+                                  0, None, ms) == fkv.FKV_ERR_BUDGET
+
+    n = ctypes.c_size_t(0)
+    assert lib.fkv_profile_workspace(ctypes.byref(d), None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_profile_workspace(ctypes.byref(d), ctypes.byref(n)) == fkv.FKV_OK
+    n_s = -(-3 * 16 // 4)
+    assert n.value == 2 * n_s * (4 + 3) * 4
+    assert lib.fkv_profile_heads(ctypes.byref(d), x, x, None, x, n.value,
+                                 None) == fkv.FKV_ERR_NULL
+    assert lib.fkv_profile_heads(ctypes.byref(d), x, x, x, x, n.value - 4,
+                                 None) == fkv.FKV_ERR_WORKSPACE
+    assert lib.fkv_profile_heads(ctypes.byref(d), x, x, x, None, n.value,
+                                 None) == fkv.FKV_ERR_WORKSPACE
+    d.query_stride = 0
+    assert lib.fkv_profile_workspace(ctypes.byref(d), ctypes.byref(n)) == fkv.FKV_ERR_SHAPE
+
 def test_attend_workspace_query(lib):
     """The workspace figure: NULL output rejected, bad descriptors rejected,
     0 for fp32 (no balanced schedule there), and for bf16 either a positive
