@@ -24,7 +24,8 @@ Also reported (same workload): the rolling compressed cache at its settled
 size ("rolling"), head profiling over every query of a sample
 ("head_profiling"), the token-granular variant ("token_variant"), the e4m3
 cache with fp8 attention ("fp8_cache", 480P and 1080P), and the CPU oracle
-on the host ("cpu_baseline").
+on the host ("cpu_baseline": the 480P layer in full, and under "configs" the
+oracle's time on layer 0 of the other workloads, extrapolated where stated).
 
 Prints one JSON line.
 """
@@ -64,6 +65,9 @@ def parse():
                     help="cycle over the workload's first N layers (own seeds, roles and "
                          "masks) instead of copies of layer 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-configs", default="tiny_f32,1080p_layer,480p_30layers,720p_14b_40layers",
+                    help="further workloads whose oracle time is reported under "
+                         "cpu_baseline.configs (layer 0; '' to skip)")
     ap.add_argument("--no-rolling", action="store_true",
                     help="skip the rolling-cache measurement")
     ap.add_argument("--multilayer", default="480p_30layers,720p_14b_40layers",
@@ -96,6 +100,12 @@ class Layer:
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         self.out = torch.empty((w.n_q, w.num_heads, w.head_dim), dtype=dt, device="cuda")
         self.dout = torch.empty_like(self.out)
+
+
+def note(msg):
+    """One line on stderr as each stage of the run ends (stdout carries only
+    the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def clock_warmup(fn, layers, seconds, torch):
@@ -485,6 +495,51 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_reps=4):
                       f"{t_attn:.1f} s; float64 NumPy"}
 
 
+
+def cpu_baseline_config(name, W, rows=(64, 256), seed=11):
+    """The oracle as it stands on layer 0 of another configuration: the
+    compression (scoring, selection, compaction) timed in full, the attention
+    of two seeded samples of query rows fitted as a + b * rows (the per-head
+    conversion of the compressed rows is the fixed part a) and taken at every
+    row.  Small workloads are timed in full.  A multi-layer pass is its
+    layer count times layer 0 ("extrapolated")."""
+    from oracle import forcing_kv as O
+    w = W.WORKLOADS[name]
+    inp = W.generate_layer(w, 0)
+    t0 = time.perf_counter()
+    c = O.compress(inp.q, inp.k, inp.v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                   w.tokens_per_frame, w.hist_frames, w.cur_frames, w.query_stride)
+    t_comp = time.perf_counter() - t0
+    if w.n_q <= 4 * rows[-1]:
+        t0 = time.perf_counter()
+        O.attend(inp.q, c["k_c"], c["v_c"], c["tok_off"])
+        t_attn = time.perf_counter() - t0
+        how = f"attention of all {w.n_q} query rows {t_attn:.2f} s"
+    else:
+        rng = np.random.default_rng(seed)
+        t = []
+        for n in rows:
+            sel = rng.choice(w.n_q, n, replace=False)
+            t0 = time.perf_counter()
+            O.attend(inp.q, c["k_c"], c["v_c"], c["tok_off"], rows=sel)
+            t.append(time.perf_counter() - t0)
+        b = max((t[1] - t[0]) / (rows[1] - rows[0]), 0.0)
+        a = max(t[0] - b * rows[0], 0.0)
+        t_attn = a + b * w.n_q
+        how = (f"attention of {rows[0]} and {rows[1]} sampled query rows ({t[0]:.2f} s, "
+               f"{t[1]:.2f} s) fitted as a + b*rows and taken at all {w.n_q} rows "
+               f"({t_attn:.1f} s)")
+    t_layer = t_comp + t_attn
+    out = {"workload": name, "value": w.n_q / t_layer, "unit": "query tok/s per layer",
+           "s_per_layer": t_layer,
+           "sample": f"layer 0: compress (score+select+compact) {t_comp:.1f} s in full; {how}",
+           "extrapolated": w.n_q > 4 * rows[-1] or w.num_layers > 1}
+    if w.num_layers > 1:
+        out["s_per_pass"] = t_layer * w.num_layers
+        out["sample"] += f"; pass = {w.num_layers} x layer 0"
+    del inp, c
+    return out
+
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on this workload and on the current kernel source."""
@@ -530,6 +585,7 @@ def main():
     r = measure(args.workload, args, fkv, torch, W)
     if args.profile_only:
         return
+    note(f"{args.workload}: step {r['ms_step']:.4f} ms")
     w = r["w"]
     value = w.n_q / (r["ms_step"] * 1e-3)
     attn_tflops = r["attn_flop"] / (r["ms_attend"] * 1e-3) / 1e12
@@ -582,22 +638,31 @@ def main():
             "kernels": kernel_rates(r2) if w2.dtype == "bf16" else None,
         }
         del r2
+        note(f"{args.secondary}: step {line['secondary']['ms_per_step']:.4f} ms")
     if w.dtype == "bf16" and not args.no_rolling and args.layers <= 1:
         line["rolling"] = measure_rolling(w.name, args, fkv, torch, W)
         line["head_profiling"] = measure_profile(w.name, args, fkv, torch, W)
         line["token_variant"] = measure_tokens(w.name, args, fkv, torch, W)
         line["fp8_cache"] = [measure_fp8(n, args, fkv, torch, W)
                              for n in (w.name, args.secondary) if n]
+        note("rolling cache, head profiling, token variant, e4m3 cache done")
     if w.dtype == "bf16" and args.multilayer and args.layers <= 1:
         line["multi_layer"] = [measure_multilayer(n, args, fkv, torch, W,
                                                   reps=5 if W.WORKLOADS[n].num_layers <= 30 else 3)
                                for n in args.multilayer.split(",") if n]
+        note("multi-layer passes done")
     if w.dtype == "bf16":
         line["measured_peaks"] = measured_peaks(fkv, torch)
         line["roofline_frac_of_measured_peak"] = (
             line["roofline"]["achieved"] / line["measured_peaks"]["mfma_bf16_tflops"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"])
+        note(f"oracle on {w.name} done")
+        line["cpu_baseline"]["configs"] = []
+        for n in args.cpu_configs.split(","):
+            if n:
+                line["cpu_baseline"]["configs"].append(cpu_baseline_config(n, W))
+                note(f"oracle on layer 0 of {n} done")
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
