@@ -70,8 +70,8 @@ constexpr int kSelWavesWide = 16;
 constexpr int kPartFrames = kMaxHistFrames + kMaxCurFrames;
 
 template <int FT, int W>
-__device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int F_tot, int ft,
-                                                  int fh, float (*part)[kPartFrames], int tid,
+__device__ __forceinline__ void accumulate_masses(const float *base, int n_s, int ft, int fh,
+                                                  float (*part)[kPartFrames], int tid,
                                                   int lane, int wave) {
   if (wave * 64 >= n_s) {
     // No sampled query reaches this wave: its partial sums are 0.
@@ -135,9 +135,9 @@ __global__ __launch_bounds__(64 * W) void select_kernel(SelectArgs a) {
     const float *base = a.lse + (int64_t)di * a.n_s * a.F_tot;
     const int ft = fh + a.F_c;
     if (W == kSelWavesWide)
-      accumulate_masses<24, W>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
+      accumulate_masses<24, W>(base, a.n_s, ft, fh, part, tid, lane, wave);
     else
-      accumulate_masses<72, W>(base, a.n_s, a.F_tot, ft, fh, part, tid, lane, wave);
+      accumulate_masses<72, W>(base, a.n_s, ft, fh, part, tid, lane, wave);
     __syncthreads();
     if (wave == 0) {
       float score = -INFINITY;
@@ -205,11 +205,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void profile_kernel(ProfileArgs a) 
   const int h = blockIdx.x;
   const float *base = a.lse + (int64_t)h * a.n_s * a.F_tot;
   if (a.F_tot <= 24)
-    accumulate_masses<24, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane,
-                                     wave);
+    accumulate_masses<24, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, part, tid, lane, wave);
   else
-    accumulate_masses<72, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, a.F_tot, part, tid, lane,
-                                     wave);
+    accumulate_masses<72, kSelWaves>(base, a.n_s, a.F_tot, a.F_tot, part, tid, lane, wave);
   __syncthreads();
   if (tid < a.F_tot) {
     float sum = part[0][tid];
