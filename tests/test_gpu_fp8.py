@@ -149,3 +149,28 @@ def test_fp8_random_shapes():
         err, _, _ = run_fp8(w, W.generate_layer(w), workspace="ckv" if case % 2 else None)
         assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS, (case, err.max(),
                                                                          err.mean())
+
+
+def test_fp8_runs_repeat_bitwise():
+    """The fp8 compression and attention (rounds schedule, halved pairs merged
+    by the combine kernel) give the same bits on a second run."""
+    import torch
+    w = W.small_workload(tokens_per_frame=2000, num_heads=12, hist_frames=2, budget_m=1,
+                         num_static=4, query_stride=7, seed=59)
+    inp = W.generate_layer(w)
+    H, D = w.num_heads, w.head_dim
+    ks, vs, qs = head_scales(inp.k, H, D), head_scales(inp.v, H, D), head_scales(inp.q, H, D)
+    desc = fkv.desc_for(w)
+    q, k, v = fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v)
+    got = []
+    for _ in range(2):
+        ckv = fkv.CompressedKV(desc, inp.head_role, inp.static_keep_mask, w.budget_m, fp8=True)
+        fkv.fkv_compress_fp8(desc, q, k, v, inp.head_role, inp.static_keep_mask, w.budget_m,
+                             ks, vs, ckv)
+        out = torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda")
+        G.announce(f"fkv_attend_fp8 {w.name} repeat")
+        fkv.fkv_attend_fp8(desc, q, ckv, qs, ks, vs, out, "ckv")
+        torch.cuda.synchronize()
+        got.append((fkv.to_host(ckv.k), fkv.to_host(ckv.v), fkv.to_host(out)))
+    for a, b in zip(*got):
+        assert np.array_equal(a, b)

@@ -239,6 +239,50 @@ def test_rounds_schedule(T, H, Fh, Fc, seed):
     assert np.max(np.abs(outs[0] - outs[1])) <= 2e-2
 
 
+
+def test_rounds_schedule_changes_only_the_halved_pairs():
+    """Each attention schedule gives the same bits on every run, and the
+    rounds schedule touches only the pairs it halves.  Workgroup b runs on
+    XCD b % 8; XCD x takes the contiguous eighth [p_lo, p_lo + n) of the
+    (head, 128-query tile) pairs, runs them in rounds of slots = 2 * CUs / 8
+    workgroups and halves the last s of them, s = rem if 2 rem <= slots else
+    slots - rem (rem = n mod slots), so that the last round is full.  Every
+    other pair must equal the one-workgroup-per-pair result bit for bit."""
+    import torch
+    w = W.small_workload(tokens_per_frame=2000, num_heads=12, hist_frames=2, cur_frames=3,
+                         budget_m=2, num_static=0, query_stride=7, seed=44)
+    inp = W.generate_layer(w)
+    desc = fkv.desc_for(w)
+    q, k, v = (fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v))
+    ws = fkv.attend_workspace(desc)
+    outs = []
+    for workspace in (ws, None):
+        runs = [fkv.to_host(G.run_attend_dense(desc, q, k, v, w.n_q, w.num_heads, w.head_dim,
+                                               w.dtype, workspace)) for _ in range(2)]
+        assert np.array_equal(runs[0], runs[1]), "two runs of one schedule differ"
+        outs.append(runs[0])
+    ntq = -(-w.n_q // 128)
+    pairs = ntq * w.num_heads
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count // 8
+    assert pairs > 8 * slots   # more pairs than resident workgroups: rounds
+    halved = set()
+    for x in range(8):
+        p_lo = pairs * x // 8
+        n = pairs * (x + 1) // 8 - p_lo
+        rem = n % slots
+        s = 0 if rem == 0 else (rem if 2 * rem <= slots else slots - rem)
+        halved.update(range(p_lo + n - s, p_lo + n))
+    assert 0 < len(halved) < pairs
+    changed = 0
+    for p in range(pairs):
+        h, qt = divmod(p, ntq)
+        rows = slice(qt * 128, min((qt + 1) * 128, w.n_q))
+        if not np.array_equal(outs[0][rows, h], outs[1][rows, h]):
+            assert p in halved, f"whole pair {p} (head {h}, tile {qt}) changed"
+            changed += 1
+    G.announce(f"{changed} of {len(halved)} halved pairs differ in some bit; "
+               f"{pairs - len(halved)} whole pairs identical")
+
 def test_attend_workspace_too_small_is_rejected():
     w = W.small_workload(tokens_per_frame=20, num_heads=2, hist_frames=3, seed=35)
     inp = W.generate_layer(w)

@@ -192,3 +192,27 @@ def test_compress_tokens_random_shapes():
         G.announce(f"token sweep case {case}: {w} S={cfg.sink_frames} R={cfg.recent_frames} "
                    f"C={cfg.budget_tokens} L={cfg.boundary_tokens}")
         run_tokens(w, W.generate_layer(w), cfg)
+
+
+def test_compress_tokens_repeats_bitwise():
+    """The token-granular compression (radix select with LDS atomics, scores
+    read from memory past the LDS limit) gives the same rows and indices on a
+    second run."""
+    import torch
+    w = W.small_workload(name="tokens_repeat", tokens_per_frame=2050, num_heads=4,
+                         hist_frames=16, num_static=2, query_stride=11, seed=49)
+    inp = W.generate_layer(w)
+    cfg = fkv.FkvTokenCfg(2, 1, 5 * 2050 + 17, 300)
+    desc = fkv.desc_for(w)
+    q, k, v = fkv.to_device(inp.q), fkv.to_device(inp.k), fkv.to_device(inp.v)
+    got = []
+    for _ in range(2):
+        ckv = fkv.CompressedKV(desc, inp.head_role, None, 0, token_cfg=cfg)
+        src = torch.empty(ckv.kept_tokens, dtype=torch.int32, device="cuda")
+        G.announce(f"fkv_compress_tokens {w.name} repeat")
+        fkv.fkv_compress_tokens(desc, cfg, q, k, v, inp.head_role, ckv, src)
+        torch.cuda.synchronize()
+        got.append((fkv.to_host(src), fkv.to_host(ckv.k), fkv.to_host(ckv.v),
+                    fkv.to_host(ckv.tok_off)))
+    for a, b in zip(*got):
+        assert np.array_equal(a, b)
