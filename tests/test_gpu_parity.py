@@ -318,6 +318,27 @@ def test_random_shapes_sweep():
         full_case(w, W.generate_layer(w))
 
 
+
+def test_random_wide_windows_sweep():
+    """Ten seeded random configurations with long windows (up to 40 history
+    and 8 current frames, so windows past 24 frames take the selection's
+    4-wave path), frames up to 300 tokens and up to 12 heads, bf16 and fp32
+    with D 64 or 128: the same checks as the sweep above."""
+    rng = np.random.default_rng(77001)
+    for case in range(10):
+        dtype = "f32" if case % 4 == 3 else "bf16"
+        D = 128 if dtype == "bf16" else int(rng.choice([64, 128]))
+        Fh, H = int(rng.integers(0, 41)), int(rng.integers(1, 13))
+        w = W.small_workload(name=f"wide{case}_{dtype}", dtype=dtype, head_dim=D,
+                             tokens_per_frame=int(rng.integers(1, 301)), num_heads=H,
+                             hist_frames=Fh, cur_frames=int(rng.integers(1, 9)),
+                             query_stride=int(rng.integers(1, 13)),
+                             budget_m=int(rng.integers(0, Fh + 3)), num_static=0,
+                             seed=8000 + case)
+        w = W.dataclasses.replace(w, num_static=int(rng.integers(0, H + 1)))
+        G.announce(f"wide sweep case {case}: {w}")
+        full_case(w, W.generate_layer(w))
+
 def test_compress_timed_matches_compress():
     """The measurement helper runs the same kernels: identical cache, offsets
     and selection, and positive stage times (scoring 0 without dynamic heads)."""
