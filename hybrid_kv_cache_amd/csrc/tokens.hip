@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kLdsKeys = 24576;   // candidates staged in LDS (96 KiB)
+constexpr int kMaxPer = kLdsKeys / kSelThreads;  // candidates per thread when staged
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -303,7 +304,30 @@ __global__ __launch_bounds__(kSelThreads) void token_select_kernel(TokenArgs a) 
     int gt_b = block_excl_scan(gt, wsum, &gt_total);
     int eq_b = block_excl_scan(eq, wsum, &eq_total);
     if (all) {
-      for (int j = lo; j < hi; ++j) out[pos + j] = a.cand_lo + j;
+      for (int j = tid; j < n; j += kSelThreads) out[pos + j] = a.cand_lo + j;
+    } else if (!none && in_lds) {
+      // This thread's keys into registers, then the key array becomes the
+      // staging of the kept indices in row order, copied out coalesced.
+      uint32_t kr[kMaxPer];
+#pragma unroll
+      for (int i = 0; i < kMaxPer; ++i) kr[i] = lo + i < hi ? lds_keys[lo + i] : 0u;
+      __syncthreads();
+      int32_t *stage = reinterpret_cast<int32_t *>(lds_keys);
+#pragma unroll
+      for (int i = 0; i < kMaxPer; ++i) {
+        if (lo + i < hi) {
+          const int row = gt_b + min(eq_b, remaining);
+          if (kr[i] > thr) {
+            stage[row] = a.cand_lo + lo + i;
+            ++gt_b;
+          } else if (kr[i] == thr) {
+            if (eq_b < remaining) stage[row] = a.cand_lo + lo + i;
+            ++eq_b;
+          }
+        }
+      }
+      __syncthreads();
+      for (int r = tid; r < c; r += kSelThreads) out[pos + r] = stage[r];
     } else if (!none) {
       for (int j = lo; j < hi; ++j) {
         const uint32_t key = key_at(j);
