@@ -38,35 +38,48 @@ __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
 
-// 1024 threads per dynamic head: dim d = tid % D, group g = tid / D takes
-// the sampled rows g, g + G, g + 2G, ... (G = 1024 / D groups, four running
-// sums in flight); the groups' partial sums are then added in group order.
+// 1024 threads per dynamic head.  Each sampled row is read as 16-byte
+// pieces: tpr = D / vec threads per row (vec elements each), R = 1024 / tpr
+// row groups; group g takes the sampled rows g, g + R, g + 2R, ... (four
+// rows in flight, added in row order).  The groups' partial sums are then
+// added per dimension in group order.
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void qsum_kernel(TokenArgs a) {
-  __shared__ float part[kSelThreads];
+  constexpr int vec = 16 / sizeof(T);
+  __shared__ float part[kSelThreads * vec];   // [R][D]
   const int di = blockIdx.x, h = a.dyn_heads[di];
-  const int tid = threadIdx.x, D = a.D, G = kSelThreads / D;
-  const int d = tid % D, g = tid / D;
+  const int tid = threadIdx.x, D = a.D;
+  const int tpr = D / vec, R = kSelThreads / tpr;
+  const int c = tid % tpr, g = tid / tpr;
   const int64_t hd = (int64_t)a.H * D;
   const int n_s = (a.n_q + a.stride - 1) / a.stride;
-  const T *q = reinterpret_cast<const T *>(a.q) + (int64_t)h * D + d;
-  const int64_t step = (int64_t)G * a.stride * hd;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  const int64_t step = (int64_t)R * a.stride * hd;
+  const T *p = reinterpret_cast<const T *>(a.q) + (int64_t)g * a.stride * hd + (int64_t)h * D +
+               c * vec;
+  float s[vec];
+#pragma unroll
+  for (int e = 0; e < vec; ++e) s[e] = 0.f;
+  auto add = [&](const u32x4 &x) {
+    const T *v = reinterpret_cast<const T *>(&x);
+#pragma unroll
+    for (int e = 0; e < vec; ++e) s[e] += to_f32<T>(v[e]);
+  };
   int j = g;
-  const T *p = q + (int64_t)g * a.stride * hd;
-  for (; j + 3 * G < n_s; j += 4 * G, p += 4 * step) {
-    s0 += to_f32<T>(p[0]);
-    s1 += to_f32<T>(p[step]);
-    s2 += to_f32<T>(p[2 * step]);
-    s3 += to_f32<T>(p[3 * step]);
+  for (; j + 3 * R < n_s; j += 4 * R, p += 4 * step) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4 *>(p + u * step);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(x[u]);
   }
-  for (; j < n_s; j += G, p += step) s0 += to_f32<T>(p[0]);
-  part[tid] = (s0 + s1) + (s2 + s3);
+  for (; j < n_s; j += R, p += step) add(*reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+  for (int e = 0; e < vec; ++e) part[g * D + c * vec + e] = s[e];
   __syncthreads();
-  if (g == 0) {
-    float s = part[d];
-    for (int k = 1; k < G; ++k) s += part[k * D + d];
-    a.qsum[di * D + d] = s;
+  if (tid < D) {
+    float t = part[tid];
+    for (int k = 1; k < R; ++k) t += part[k * D + tid];
+    a.qsum[di * D + tid] = t;
   }
 }
 
