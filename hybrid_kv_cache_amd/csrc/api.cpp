@@ -13,6 +13,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdint>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -48,6 +50,22 @@ fkv_status_t ok() {
 }
 
 int elt_bytes(int32_t dtype) { return dtype == FKV_BF16 ? 2 : 4; }
+
+// The kernels move 16-byte pieces of every tensor and workspace they read or
+// write, so those must start on a 16-byte boundary (NULL passes here; the
+// NULL checks are separate).
+fkv_status_t check_aligned(std::initializer_list<const void *> ptrs, const char *what) {
+  for (const void *ptr : ptrs)
+    if (reinterpret_cast<uintptr_t>(ptr) & 15u)
+      return fail(FKV_ERR_SHAPE, "%s: a pointer is not 16-byte aligned", what);
+  return FKV_OK;
+}
+
+// The query block and the plain window of a compression.
+fkv_status_t check_inputs(const void *q, const void *k_cache, const void *v_cache) {
+  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  return check_aligned({q, k_cache, v_cache}, "q, k_cache or v_cache");
+}
 
 float log2e_scale(const fkv_desc_t &d) {
   const float scale = d.scale != 0.f ? d.scale : 1.0f / std::sqrt((float)d.head_dim);
@@ -271,6 +289,9 @@ hipError_t side_stream(SideStream **out, std::unique_lock<std::mutex> *lock) {
 fkv_status_t attend_common(const fkv_desc_t *d, const void *q, const void *k, const void *v,
                            const int64_t *tok_off, void *out, void *workspace,
                            size_t workspace_bytes, void *stream) {
+  const fkv_status_t st =
+      check_aligned({q, k, v, out, workspace}, "q, k, v, out or the attention workspace");
+  if (st != FKV_OK) return st;
   if (workspace && d->dtype == FKV_BF16) {
     const size_t need = fkv::attend_part_bytes();
     if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
@@ -306,6 +327,8 @@ fkv_status_t check_compress_out(const Plan &p, const void *q, const fkv_ckv_t *o
   if (!out) return fail(FKV_ERR_NULL, "out (fkv_ckv_t) is NULL");
   if (!out->k || !out->v || !out->tok_off || !out->seg_off || (!out->seg_idx && p.Fh > 0))
     return fail(FKV_ERR_NULL, "a compressed-cache buffer (k, v, tok_off, seg_idx, seg_off) is NULL");
+  const fkv_status_t st = check_aligned({q, out->k, out->v}, "q or the compressed cache's k, v");
+  if (st != FKV_OK) return st;
   if (out->cap_tokens < p.tok_off[p.H])
     return fail(FKV_ERR_CAPACITY, "cap_tokens %lld < %lld rows needed",
                 (long long)out->cap_tokens, (long long)p.tok_off[p.H]);
@@ -358,6 +381,8 @@ fkv_status_t compress_common(const fkv_desc_t *desc, const Plan &p, const void *
   if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
     return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
+  st = check_aligned({workspace}, "workspace");
+  if (st != FKV_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char *ws = reinterpret_cast<char *>(workspace);
@@ -644,7 +669,8 @@ fkv_status_t fkv_compress(const fkv_desc_t *desc, const void *q, const void *k_c
   Plan p;
   fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
                          workspace_bytes, stream, nullptr, nullptr, true);
 }
@@ -658,8 +684,11 @@ fkv_status_t fkv_compress_attend(const fkv_desc_t *desc, const void *q, const vo
   Plan p;
   fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   if (!attend_out) return fail(FKV_ERR_NULL, "attend_out is NULL");
+  st = check_aligned({attend_out, attend_workspace}, "attend_out or attend_workspace");
+  if (st != FKV_OK) return st;
   st = check_compress_out(p, q, out);
   if (st != FKV_OK) return st;
   if (workspace_bytes < p.ws_bytes || (p.ws_bytes > 0 && !workspace))
@@ -700,7 +729,8 @@ fkv_status_t fkv_compress_noalloc(const fkv_desc_t *desc, const void *q, const v
   Plan p;
   fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   st = check_compress_out(p, q, out);
   if (st != FKV_OK) return st;
   if (p.ws_bytes > fkv::kScratchBytes)
@@ -739,7 +769,8 @@ fkv_status_t fkv_compress_fp8(const fkv_desc_t *desc, const void *q, const void 
   if (st != FKV_OK) return st;
   st = check_scales(desc, kv_scales, 2 * desc->num_heads, "kv_scales");
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   return compress_common(desc, p, q, plain_window(desc, k_cache, v_cache), out, workspace,
                          workspace_bytes, stream, kv_scales, nullptr, true);
 }
@@ -754,6 +785,9 @@ fkv_status_t fkv_attend_fp8(const fkv_desc_t *desc, const void *q, const fkv_ckv
   if (!q || !out) return fail(FKV_ERR_NULL, "q or out is NULL");
   if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
     return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  st = check_aligned({q, out, ckv->k, ckv->v, workspace},
+                     "q, out, the cache's k, v or the attention workspace");
+  if (st != FKV_OK) return st;
   if (workspace) {
     const size_t need = fkv::attend_part_bytes();
     if (need == 0) return fail(FKV_ERR_HIP, "no HIP device to size the attention workspace for");
@@ -790,7 +824,8 @@ fkv_status_t fkv_compress_timed(const fkv_desc_t *desc, const void *q, const voi
   Plan p;
   fkv_status_t st = make_plan(desc, nullptr, head_role, static_keep_mask, budget_m, &p);
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   if (!ms) return fail(FKV_ERR_NULL, "ms is NULL");
   hipEvent_t ev[4] = {};
   for (int i = 0; i < 4; ++i) {
@@ -839,6 +874,8 @@ fkv_status_t fkv_compress_ragged(const fkv_desc_t *desc, const void *q, const fk
   if (!hist || !hist->k || !hist->v || !hist->tok_off)
     return fail(FKV_ERR_NULL, "history cache (k, v, tok_off) is NULL");
   if (!cur_k || !cur_v) return fail(FKV_ERR_NULL, "cur_k or cur_v is NULL");
+  st = check_aligned({hist->k, hist->v, cur_k, cur_v}, "the history's k, v, cur_k or cur_v");
+  if (st != FKV_OK) return st;
   if (out && (out->k == hist->k || out->v == hist->v || out->tok_off == hist->tok_off))
     return fail(FKV_ERR_SHAPE, "out must not share buffers with the history cache");
   fkv::WinView win = plain_window(desc, hist->k, hist->v);
@@ -856,6 +893,8 @@ fkv_status_t fkv_refresh_current(const fkv_desc_t *desc, const void *cur_k, cons
   if (!cur_k || !cur_v) return fail(FKV_ERR_NULL, "cur_k or cur_v is NULL");
   if (!ckv || !ckv->k || !ckv->v || !ckv->tok_off)
     return fail(FKV_ERR_NULL, "compressed cache (k, v, tok_off) is NULL");
+  st = check_aligned({cur_k, cur_v, ckv->k, ckv->v}, "cur_k, cur_v or the cache's k, v");
+  if (st != FKV_OK) return st;
   fkv::CompactArgs ca;
   ca.slots = nullptr;
   ca.win = plain_window(desc, nullptr, nullptr);
@@ -925,15 +964,20 @@ fkv_status_t fkv_compress_tokens(const fkv_desc_t *desc, const fkv_token_cfg_t *
   TokenPlan p;
   fkv_status_t st = make_token_plan(desc, cfg, head_role, &p);
   if (st != FKV_OK) return st;
-  if (!q || !k_cache || !v_cache) return fail(FKV_ERR_NULL, "q, k_cache or v_cache is NULL");
+  st = check_inputs(q, k_cache, v_cache);
+  if (st != FKV_OK) return st;
   if (!out || !out->k || !out->v || !out->tok_off)
     return fail(FKV_ERR_NULL, "a compressed-cache buffer (k, v, tok_off) is NULL");
   if (out->cap_tokens < p.tok_off[p.H])
     return fail(FKV_ERR_CAPACITY, "cap_tokens %lld < %lld rows needed",
                 (long long)out->cap_tokens, (long long)p.tok_off[p.H]);
+  st = check_aligned({out->k, out->v}, "the compressed cache's k, v");
+  if (st != FKV_OK) return st;
   if (!workspace || workspace_bytes < p.ws_bytes)
     return fail(FKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
+  st = check_aligned({workspace}, "workspace");
+  if (st != FKV_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // The plan's offsets reach the device as kernel arguments; the selection
   // kernel writes them to out->tok_off.
@@ -991,6 +1035,8 @@ fkv_status_t fkv_profile_heads(const fkv_desc_t *desc, const void *q, const void
   fkv_status_t st = check_desc(desc);
   if (st != FKV_OK) return st;
   if (!q || !k_cache || !mass_accum) return fail(FKV_ERR_NULL, "q, k_cache or mass_accum is NULL");
+  st = check_aligned({q, k_cache, workspace}, "q, k_cache or workspace");
+  if (st != FKV_OK) return st;
   size_t need = 0;
   fkv_profile_workspace(desc, &need);
   if (!workspace || workspace_bytes < need)

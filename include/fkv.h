@@ -24,6 +24,11 @@
  * Limits: 1 <= H <= 64, 0 <= F_h <= 64, 1 <= F_c <= 8, 1 <= T, s >= 1,
  *         N_win < 2^31, each window tensor (N_win * H * D elements) below
  *         4 GiB; element offsets are computed in 64 bits.
+ * Alignment: the kernels move 16-byte pieces, so every tensor (q, k_cache,
+ *         v_cache, out, the compressed cache's k and v, cur_k, cur_v) and
+ *         every workspace must start on a 16-byte boundary, else
+ *         FKV_ERR_SHAPE; offset and index arrays need only their natural
+ *         alignment.
  *
  * Threading and streams: calls are stateless apart from the thread-local
  * error string (and the scratch array of fkv_compress_noalloc); every device

@@ -315,6 +315,53 @@ def test_compress_fp8_timed_and_profile_argument_errors(lib):
     d.query_stride = 0
     assert lib.fkv_profile_workspace(ctypes.byref(d), ctypes.byref(n)) == fkv.FKV_ERR_SHAPE
 
+
+def test_misaligned_tensors_are_rejected(lib):
+    """Every entry point refuses a tensor or workspace that does not start on
+    a 16-byte boundary (the kernels move 16-byte pieces), on the host, before
+    any HIP call: FKV_ERR_SHAPE with the text naming the argument group."""
+    d = fkv.make_desc(2, 128, 16, 4, 3, 4)
+    role = np.array([0, 1], np.uint8)
+    mask = np.ones((2, 4), np.uint8)
+    r, m = role.ctypes.data, mask.ctypes.data
+    A, X = 0x1000, 0x1008    # aligned, misaligned by 8 bytes
+    ckv = fkv.FkvCkv(A, A, A, A, A, A, 1 << 20)
+    bad_k = fkv.FkvCkv(X, A, A, A, A, A, 1 << 20)
+    scales = np.ones(3 * 2, np.float32)
+    cfg = fkv.FkvTokenCfg(1, 1, 8, 2)
+    hist_frames = np.array([4, 4], np.int32)
+    calls = [
+        lambda: lib.fkv_compress(ctypes.byref(d), X, A, A, r, m, 2, ctypes.byref(ckv), A, 1 << 20,
+                                 None),
+        lambda: lib.fkv_compress(ctypes.byref(d), A, A, A, r, m, 2, ctypes.byref(bad_k), A,
+                                 1 << 20, None),
+        lambda: lib.fkv_compress(ctypes.byref(d), A, A, A, r, m, 2, ctypes.byref(ckv), X,
+                                 1 << 20, None),
+        lambda: lib.fkv_compress_noalloc(ctypes.byref(d), A, A, X, r, m, 2, ctypes.byref(ckv),
+                                         None),
+        lambda: lib.fkv_compress_attend(ctypes.byref(d), A, A, A, r, m, 2, ctypes.byref(ckv), A,
+                                        1 << 20, X, None, 0, None),
+        lambda: lib.fkv_compress_fp8(ctypes.byref(d), A, X, A, r, m, 2, scales.ctypes.data,
+                                     ctypes.byref(ckv), A, 1 << 20, None),
+        lambda: lib.fkv_compress_ragged(ctypes.byref(d), A, ctypes.byref(ckv),
+                                        hist_frames.ctypes.data, X, A, r, m, 2,
+                                        ctypes.byref(fkv.FkvCkv(A + 16, A + 16, A + 16, A + 16,
+                                                                A + 16, A + 16, 1 << 20)),
+                                        A, 1 << 20, None),
+        lambda: lib.fkv_refresh_current(ctypes.byref(d), A, X, ctypes.byref(ckv), None),
+        lambda: lib.fkv_compress_tokens(ctypes.byref(d), ctypes.byref(cfg), A, X, A, r,
+                                        ctypes.byref(ckv), None, A, 1 << 20, None),
+        lambda: lib.fkv_attend(ctypes.byref(d), X, ctypes.byref(ckv), A, None, 0, None),
+        lambda: lib.fkv_attend(ctypes.byref(d), A, ctypes.byref(ckv), A, X, 1 << 30, None),
+        lambda: lib.fkv_attend_dense(ctypes.byref(d), A, A, X, A, None, 0, None),
+        lambda: lib.fkv_attend_fp8(ctypes.byref(d), A, ctypes.byref(ckv), scales.ctypes.data, X,
+                                   None, 0, None),
+        lambda: lib.fkv_profile_heads(ctypes.byref(d), A, A, A, X, 1 << 20, None),
+    ]
+    for i, call in enumerate(calls):
+        assert call() == fkv.FKV_ERR_SHAPE, (i, fkv.fkv_last_error())
+        assert "16-byte aligned" in fkv.fkv_last_error(), (i, fkv.fkv_last_error())
+
 def test_attend_workspace_query(lib):
     """The workspace figure: NULL output rejected, bad descriptors rejected,
     0 for fp32 (no balanced schedule there), and for bf16 either a positive
